@@ -1,0 +1,206 @@
+/*
+ * lsh.h - exact long-sequence multi-head attention forward for AMD MI355X
+ * (gfx950). C ABI of liblsh.so.
+ *
+ * What the library computes. For every batch entry b and head h, with
+ * scores s_ij = scale * <q_i, k_j>, the forward pass of softmax attention
+ *     LSE_i = log( sum_j exp(s_ij) )                (natural log)
+ *     O_i   = sum_j exp(s_ij - LSE_i) * v_j
+ * (definition: "LLM Lab Notes 05: Attention Tensor Parallelism - Splitting
+ * QKV by Head, Megatron Style", sections 2 and 3: per-head scaled dot
+ * products, softmax over the keys, weighted sum of the values; heads never
+ * interact). O is returned in float32, LSE in float32. The computation is
+ * exact up to floating-point rounding: a blockwise online softmax over key
+ * tiles of 64, with QK^T and PV on the matrix cores and fp32 accumulation.
+ *
+ * Conventions shared by every entry point.
+ *  - Pointers named q, k, v, o, lse, src, dst, o_parts, lse_parts,
+ *    block_mask and workspace are DEVICE pointers owned by the caller. The
+ *    library allocates no device memory and keeps no per-call state.
+ *  - Streams are hipStream_t values passed as void*; NULL is the null
+ *    stream. Every function only enqueues work and returns; results are
+ *    ready when the stream(s) reach that point.
+ *  - Tensors use element strides; the innermost (head_dim) stride is 1.
+ *    Q is [B, Sq, H, D] and K, V are [B, Skv, H, D] as seen through
+ *    (b, s, h) strides; O is float32 [B, Sq, H, D] through its own strides;
+ *    LSE is float32 [B, H, Sq], contiguous.
+ *  - Base pointers must be 16-byte aligned and every stride times the
+ *    element size must be a multiple of 16 bytes. D must be 128.
+ *  - Outputs must not overlap inputs or each other.
+ *  - Errors: every argument is validated before the first HIP call, so a
+ *    call that returns an error has enqueued nothing. A failed kernel
+ *    launch returns LSH_ERR_HIP. lsh_last_error() gives a message for the
+ *    last failing call on the calling thread.
+ *  - Determinism: the result for one (b, h) depends only on that head's
+ *    q, k, v, the dtype, D, Sq, Skv and scale - never on H, on the head
+ *    chunking, on strides, on streams or on the run. Repeated runs are
+ *    bit-identical; no floating-point atomics are used.
+ *  - Thread safety: all entry points may be called concurrently.
+ */
+#ifndef LSH_H
+#define LSH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LSH_ABI_VERSION 1
+#define LSH_HEAD_DIM 128     /* the only supported head_dim */
+#define LSH_MASK_BLOCK 128   /* block edge of the block-sparse mask, tokens */
+
+typedef enum lsh_status {
+  LSH_OK = 0,
+  LSH_ERR_INVALID = 1,      /* bad argument (null pointer, bad size, stride, alignment) */
+  LSH_ERR_UNSUPPORTED = 2,  /* valid but not implemented (D != 128, huge offsets) */
+  LSH_ERR_WORKSPACE = 3,    /* workspace missing or too small */
+  LSH_ERR_NO_DEVICE = 4,    /* no gfx950 device is current */
+  LSH_ERR_HIP = 5           /* a HIP runtime call or kernel launch failed */
+} lsh_status;
+
+typedef enum lsh_dtype {
+  LSH_F32 = 0,   /* float32 Q, K, V */
+  LSH_BF16 = 1   /* bfloat16 Q, K, V (fp32 accumulation and output) */
+} lsh_dtype;
+
+typedef void* lsh_stream;   /* a hipStream_t */
+
+/* Arguments of one attention forward. */
+typedef struct lsh_attn_args {
+  const void* q;          /* [B, Sq, H, D] elements of `dtype` */
+  const void* k;          /* [B, Skv, H, D] */
+  const void* v;          /* [B, Skv, H, D] */
+  float* o;               /* float32 [B, Sq, H, D] */
+  float* lse;             /* float32 [B, H, Sq], contiguous */
+  int32_t dtype;          /* lsh_dtype */
+  int32_t reserved;       /* must be 0 */
+  int64_t B, Sq, Skv, H, D;
+  int64_t q_stride[3];    /* element strides of (b, s, h) */
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+  float scale;            /* score multiplier; 1/sqrt(D) for standard attention */
+} lsh_attn_args;
+
+/* Version of this header the library was built from (LSH_ABI_VERSION). */
+int lsh_abi_version(void);
+
+/* Static text for a status code. */
+const char* lsh_status_str(int status);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* lsh_last_error(void);
+
+/* LSH_OK when a gfx950 device is current on the calling thread, else
+ * LSH_ERR_NO_DEVICE. */
+lsh_status lsh_device_check(void);
+
+/*
+ * Dense attention forward over all keys, launched on one stream.
+ * Reads Q, K, V through their strides, writes O and LSE. Skv >= 1.
+ * Source: the TP page above, sections 2-3 (per-head local attention).
+ */
+lsh_status lsh_attn_fwd(const lsh_attn_args* args, lsh_stream stream);
+
+/*
+ * Head-chunked multi-stream forward.
+ * Source: "HCMS: Head-Chunked Multi-Stream Pipeline for Communication-
+ * Computation Overlap in Long-Sequence Parallel Attention", Abstract: the
+ * heads are split into chunks, possibly of unequal size; the re-layout of
+ * one chunk (an all-to-all across GPUs there, a local head-major copy here)
+ * runs on a second stream while the attention of the previous chunk runs,
+ * and the result is the same as the unchunked computation.
+ *
+ * head_chunks[0..n_chunks-1] >= 1 and sum to H; chunk c covers heads
+ * [sum_{c'<c}, sum_{c'<=c}) in ascending order. For each chunk, Q, K and V
+ * of its heads are copied by lsh_head_permute into the workspace as
+ * [B, hc, S, D] (on `permute_stream`), then attention runs on that copy
+ * (on `compute_stream`) and writes the chunk's heads of O and LSE.
+ * Ordering: the permute stream first waits for all work previously
+ * enqueued on the compute stream; chunk c's attention waits for chunk c's
+ * copy; all the call's work is ordered before later work on the compute
+ * stream. The two streams may be the same stream. Requires Sq == Skv.
+ * O and LSE are bit-identical to lsh_attn_fwd on the same inputs.
+ * workspace: device memory of at least lsh_attn_fwd_chunked_workspace(args)
+ * bytes; it must not be reused before the compute stream has passed this
+ * call's work.
+ */
+lsh_status lsh_attn_fwd_chunked(const lsh_attn_args* args,
+                                const int32_t* head_chunks, int32_t n_chunks,
+                                void* workspace, size_t workspace_bytes,
+                                lsh_stream compute_stream,
+                                lsh_stream permute_stream);
+
+/* Workspace bytes of lsh_attn_fwd_chunked: the head-major copies of Q, K
+ * and V (3 * B * H * S * D elements), 256-byte aligned. 0 on bad args. */
+size_t lsh_attn_fwd_chunked_workspace(const lsh_attn_args* args);
+
+/*
+ * Attention of the queries against ONE block of keys (one Ring Attention
+ * round). Source: "CHARM+: How Cross-Hardware Attention Breaks Through
+ * Distributed Communication Bottlenecks", section on where the bottleneck
+ * comes from: in Ring Attention each device keeps its queries, receives the
+ * KV blocks in turn and combines per-block partial results.
+ * O is normalised over the block's keys and LSE is the block's log-sum-exp,
+ * so lsh_lse_merge over all blocks yields attention over all keys.
+ * Skv may be 0 (an empty block): O = 0 and LSE = -inf; k and v may then be
+ * NULL.
+ */
+lsh_status lsh_attn_partial(const lsh_attn_args* args, lsh_stream stream);
+
+/*
+ * Merge n partial results over disjoint key sets (same page as above; the
+ * "Re-Merge" of "CHARM+: Cross-Hardware Attention with Re-Merge Multistream
+ * Mechanism", read as this merge):
+ *   M = max_k LSE_k, w_k = exp(LSE_k - M), Z = sum_k w_k,
+ *   LSE = M + log Z,  O = sum_k (w_k / Z) * O_k.
+ * Rows whose n LSE values are all -inf get O = 0 and LSE = -inf.
+ * o_parts: float32 [n, B, Sq, H, D] contiguous; lse_parts: float32
+ * [n, B, H, Sq] contiguous; o: float32 [B, Sq, H, D] contiguous; lse:
+ * float32 [B, H, Sq] contiguous. 1 <= n <= 4096. D must be 128.
+ */
+lsh_status lsh_lse_merge(const float* o_parts, const float* lse_parts,
+                         int32_t n, int64_t B, int64_t Sq, int64_t H,
+                         int64_t D, float* o, float* lse, lsh_stream stream);
+
+/*
+ * Head-major copy of heads [h0, h0 + hc): src [B, S, H, D] (contiguous) ->
+ * dst [B, hc, S, D] (contiguous), dst[b, h - h0, s, :] = src[b, s, h, :].
+ * A bit copy. It stands in, on one GPU, for the all-to-all that turns a
+ * sequence-sharded layout into a head-sharded one (HCMS page, Abstract;
+ * "db-SP: Accelerating Sparse Attention for Visual Generative Models with
+ * Dual-Balanced Sequence Parallelism", Abstract: Ulysses parallelises
+ * along the head dimension). D * element size must be a multiple of 16.
+ */
+lsh_status lsh_head_permute(const void* src, void* dst, int32_t dtype,
+                            int64_t B, int64_t S, int64_t H, int64_t D,
+                            int32_t h0, int32_t hc, lsh_stream stream);
+
+/*
+ * Block-sparse attention forward. Source: the db-SP page, Abstract:
+ * block-wise sparse attention computes only the dense blocks of a sparse
+ * mask; sparsity differs between heads and dense blocks sit irregularly.
+ * block_mask: device uint8 [B, H, ceil(Sq/128), ceil(Skv/128)]; query i
+ * attends key j iff block_mask[b, h, i/128, j/128] != 0. Masked pairs are
+ * excluded from the softmax. A query row with no kept block gets O = 0 and
+ * LSE = -inf. Requires a bf16 or f32 args as lsh_attn_fwd, Skv >= 1.
+ * workspace: at least lsh_attn_fwd_blocksparse_workspace(args) bytes; it
+ * holds the per-(b, h, query-block) kept-block counts and the work order
+ * (query blocks sorted by decreasing kept count, so the heaviest start
+ * first). Same reuse rule as the chunked workspace.
+ */
+lsh_status lsh_attn_fwd_blocksparse(const lsh_attn_args* args,
+                                    const uint8_t* block_mask,
+                                    void* workspace, size_t workspace_bytes,
+                                    lsh_stream stream);
+
+/* Workspace bytes of lsh_attn_fwd_blocksparse. 0 on bad args. */
+size_t lsh_attn_fwd_blocksparse_workspace(const lsh_attn_args* args);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSH_H */

@@ -1,0 +1,584 @@
+// Blockwise online-softmax attention forward for gfx950 (MI355X).
+//
+// What is computed: for each (b, h) and query row i,
+//   LSE_i = log(sum_j exp(scale * <q_i, k_j>)),
+//   O_i   = sum_j exp(scale * <q_i, k_j> - LSE_i) * v_j,
+// the per-head scaled dot-product attention of "LLM Lab Notes 05: Attention
+// Tensor Parallelism - Splitting QKV by Head, Megatron Style" (sections 2
+// and 3), over all keys (dense) or over the kept 128x128 blocks of a block
+// mask (block-wise sparse attention, "db-SP: Accelerating Sparse Attention
+// for Visual Generative Models with Dual-Balanced Sequence Parallelism",
+// Abstract).
+//
+// Design (one wavefront = 32 query rows; a workgroup = WAVES wavefronts
+// sharing each key tile through LDS):
+//  * Q of the wavefront's 32 rows stays in VGPRs for the whole key loop.
+//  * Key tiles of 64 keys: K and V are staged HBM -> VGPR -> LDS, double
+//    buffered, one barrier per tile. K rows are XOR-swizzled by 16-byte
+//    chunk so the QK^T operand reads are bank-conflict free; V rows use a
+//    different swizzle matched to the transposing reads below.
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: the accumulator puts one
+//    query per lane (lane l and l+32 share query l%32 and split the keys),
+//    so the row max and row sum need one cross-half swap only
+//    (v_permlane32_swap), and the exponentiated scores are already laid
+//    out as the B operand of the next product.
+//  * O^T += V^T P^T on the same MFMA. V^T comes straight from the
+//    row-major V tile with ds_read_b64_tr_b16, which returns, per lane, 4
+//    keys of one head_dim column.
+//  * Online softmax in the log2 domain with a lazy rescale: the running
+//    max only moves when a tile's max exceeds it by more than 2^8 in
+//    probability, so P stays <= 256 and the O rescale is skipped on almost
+//    every tile. Each query's arithmetic depends only on its own scores,
+//    so results do not depend on the workgroup size, the grid order, the
+//    number of heads or the strides.
+//  * fp32 inputs use v_mfma_f32_32x32x2_f32 with the same structure and P
+//    kept in fp32.
+#include "lsh_internal.hpp"
+
+#include <cstdlib>
+#include <cstring>
+
+namespace lsh {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kNegInf = -__builtin_inff();
+// Lazy-rescale threshold in log2 units: the running max is replaced only
+// when a new score exceeds it by more than this.
+constexpr float kRescaleLog2 = 8.0f;
+
+// 16-byte chunk swizzles inside a 256-byte (128 x bf16) LDS row.
+__device__ __forceinline__ int swz_k(int row, int c) { return c ^ (row & 15); }
+__device__ __forceinline__ int swz_v(int row, int c) {
+  return c ^ (((row & 3) << 2) | ((row >> 2) & 3));
+}
+
+// Workgroups are handed to the 8 XCDs round-robin; remap so that each XCD
+// walks a contiguous range of (b, h, query-block) items and the K/V stream
+// of a head is shared inside one XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  constexpr int X = 8;
+  const int per = n / X, rem = n % X;
+  const int x = bid % X, k = bid / X;
+  return x < rem ? x * (per + 1) + k : rem * (per + 1) + (x - rem) * per + k;
+}
+
+// Value of lane l^32 (the other half of the wavefront) for both halves:
+// r[0] + r[1] / max(r[0], r[1]) combine the two halves.
+__device__ __forceinline__ float pair_max(float x) {
+  unsigned u = __builtin_bit_cast(unsigned, x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  unsigned u = __builtin_bit_cast(unsigned, x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+__device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0; }
+
+// Item -> (b, h, query block) and the per-item key-tile list.
+struct Item {
+  int b, h, qblk;
+};
+
+__device__ __forceinline__ Item decode_item(int item, int n_qblk, int H) {
+  Item it;
+  it.qblk = item % n_qblk;
+  const int bh = item / n_qblk;
+  it.h = bh % H;
+  it.b = bh / H;
+  return it;
+}
+
+// Builds, in LDS, the ascending list of kept key blocks of one mask row.
+// Returns the number of kept blocks (same value in every thread).
+template <int NT>
+__device__ int build_kept_list(const uint8_t* mrow, int n_mkb, unsigned short* kept,
+                               int* wave_cnt) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int W = NT / 64;
+  int total = 0;
+  for (int base = 0; base < n_mkb; base += NT) {
+    const int j = base + tid;
+    const bool flag = j < n_mkb && mrow[j] != 0;
+    const unsigned long long bal = __ballot(flag);
+    const int below = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wave_cnt[wave] = __builtin_popcountll(bal);
+    __syncthreads();
+    int before = 0, sum = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const int c = wave_cnt[w];
+      before += (w < wave) ? c : 0;
+      sum += c;
+    }
+    if (flag) kept[total + before + below] = (unsigned short)j;
+    total += sum;
+    __syncthreads();
+  }
+  return total;
+}
+
+// Start key of tile t: dense tiles are consecutive; sparse tiles are the two
+// 64-key halves of each kept 128-key block.
+template <bool SPARSE>
+__device__ __forceinline__ int tile_key0(int t, const unsigned short* kept) {
+  if constexpr (SPARSE) {
+    return (int)kept[t >> 1] * kMaskBlock + (t & 1) * kBN;
+  } else {
+    return t * kBN;
+  }
+}
+
+// ----------------------------------------------------------------- bf16 path
+
+template <int WAVES, bool SPARSE>
+__global__ __launch_bounds__(WAVES * 64) void attn_fwd_bf16_kernel(AttnParams p) {
+  constexpr int NT = WAVES * 64;
+  constexpr int BM = WAVES * kQW;
+  constexpr int CPT = kBN * (kD / 8) / NT;  // 16-byte chunks per thread per tensor
+  static_assert(CPT >= 1 && CPT * NT == kBN * (kD / 8), "tile/threads mismatch");
+  static_assert(!SPARSE || BM == kMaskBlock, "sparse kernel works on one mask row");
+
+  __shared__ __attribute__((aligned(16))) __bf16 lds_k[2][kBN * kD];
+  __shared__ __attribute__((aligned(16))) __bf16 lds_v[2][kBN * kD];
+  extern __shared__ unsigned short kept_dyn[];
+  __shared__ int wave_cnt[WAVES];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  int item;
+  if constexpr (SPARSE) {
+    item = p.order ? p.order[blockIdx.x] : (int)blockIdx.x;
+  } else {
+    item = xcd_remap(blockIdx.x, gridDim.x);
+  }
+  const Item it = decode_item(item, p.n_qblk, p.H);
+  const int q0 = it.qblk * BM;
+  const int qi = q0 + wave * kQW + l32;
+  const bool q_ok = qi < p.Sq;
+
+  const __bf16* qp = static_cast<const __bf16*>(p.q) + it.b * p.q_sb + it.h * p.q_sh;
+  const __bf16* kp = static_cast<const __bf16*>(p.k) + it.b * p.k_sb + it.h * p.k_sh;
+  const __bf16* vp = static_cast<const __bf16*>(p.v) + it.b * p.v_sb + it.h * p.v_sh;
+
+  int n_tiles;
+  const unsigned short* kept = kept_dyn;
+  if constexpr (SPARSE) {
+    const uint8_t* mrow = p.mask + (((int64_t)it.b * p.H + it.h) * p.n_mqb + it.qblk) * p.n_mkb;
+    const int n_kept = build_kept_list<NT>(mrow, p.n_mkb, kept_dyn, wave_cnt);
+    n_tiles = 2 * n_kept;
+  } else {
+    n_tiles = (p.Skv + kBN - 1) / kBN;
+  }
+
+  // Q fragments: lane holds Q[qi][16 s + 8 hh .. +7], s = 0..7.
+  bf16x8 qf[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    if (q_ok) {
+      qf[s] = *reinterpret_cast<const bf16x8*>(qp + (int64_t)qi * p.q_ss + 16 * s + 8 * hh);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qf[s][i] = (__bf16)0.0f;
+    }
+  }
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+  float m_run = kNegInf;  // running max of raw scores (both halves agree)
+  float l_run = 0.0f;     // this half's partial sum of exp2(s*c - m*c)
+  const float c = p.scale_log2;
+
+  u32x4 kst[CPT], vst[CPT];
+  auto gload = [&](int t) {
+    const int key0 = tile_key0<SPARSE>(t, kept);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int cid = tid + i * NT;
+      const int row = cid >> 4, ch = cid & 15;
+      const int key = key0 + row;
+      if (key < p.Skv) {
+        kst[i] = *reinterpret_cast<const u32x4*>(kp + (int64_t)key * p.k_ss + ch * 8);
+        vst[i] = *reinterpret_cast<const u32x4*>(vp + (int64_t)key * p.v_ss + ch * 8);
+      } else {
+        kst[i] = u32x4{0u, 0u, 0u, 0u};
+        vst[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int cid = tid + i * NT;
+      const int row = cid >> 4, ch = cid & 15;
+      *reinterpret_cast<u32x4*>(&lds_k[buf][row * kD + swz_k(row, ch) * 8]) = kst[i];
+      *reinterpret_cast<u32x4*>(&lds_v[buf][row * kD + swz_v(row, ch) * 8]) = vst[i];
+    }
+  };
+
+  if (n_tiles > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) gload(t + 1);
+
+    // ---- S^T = K Q^T for the tile's 2 key blocks of 32
+    f32x16 st[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[kb][r] = 0.0f;
+      const int row = kb * 32 + l32;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(&lds_k[buf][row * kD + swz_k(row, 2 * s + hh) * 8]);
+        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], st[kb], 0, 0, 0);
+      }
+    }
+
+    // ---- mask keys past the end (last, partial tile only)
+    const int key0 = tile_key0<SPARSE>(t, kept);
+    if (key0 + kBN > p.Skv) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key >= p.Skv) st[kb][r] = kNegInf;
+        }
+    }
+
+    // ---- row max over this lane's 32 keys, then across the two halves
+    float mx = st[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
+    mx = pair_max(mx);
+
+    // ---- lazy rescale: move the running max only on a large increase
+    const bool need = (mx - m_run) * c > kRescaleLog2;
+    if (wave_any(need)) {
+      const float m_new = need ? mx : m_run;
+      const float alpha = need ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.0f;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float mc = (m_run == kNegInf) ? 0.0f : m_run * c;
+
+    // ---- P = exp2(s c - m c), partial row sum, bf16 B operands
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][r], c, -mc));
+        l_run += e;
+        pf[kb][r >> 3][r & 7] = (__bf16)e;
+      }
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        // transposing reads: lane (16 g + 4 e + a) points at key
+        // kb*32 + jj*16 + 8 part + 4 (g/2) + e, columns 32 db + 16 (g%2) + 4 a
+        const int g = lane >> 4, e = (lane >> 2) & 3, a = lane & 3;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          s16x4 w[2];
+#pragma unroll
+          for (int part = 0; part < 2; ++part) {
+            const int row = kb * 32 + jj * 16 + 8 * part + 4 * (g >> 1) + e;
+            const int col = db * 32 + 16 * (g & 1) + 4 * a;
+            const int off = row * kD + swz_v(row, col >> 3) * 8 + (col & 7);
+            w[part] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (LDS_AS s16x4*)((LDS_AS __bf16*)(&lds_v[buf][0]) + off));
+          }
+          // whole-vector assembly: slots 0-3 from the first read, 4-7 from the second
+          const s16x8 w8 = __builtin_shufflevector(w[0], w[1], 0, 1, 2, 3, 4, 5, 6, 7);
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, w8);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][jj], acc[db], 0, 0, 0);
+        }
+      }
+
+    if (t + 1 < n_tiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: combine halves, normalise, write O and LSE
+  const float l_tot = pair_sum(l_run);
+  if (!q_ok) return;
+  float* op = p.o + it.b * p.o_sb + it.h * p.o_sh + (int64_t)qi * p.o_ss;
+  const bool empty = !(l_tot > 0.0f);
+  const float inv_l = empty ? 0.0f : 1.0f / l_tot;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = db * 32 + 8 * g4 + 4 * hh;
+      f32x4 o4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o4[i] = acc[db][4 * g4 + i] * inv_l;
+      *reinterpret_cast<f32x4*>(op + d) = o4;
+    }
+  if (hh == 0) {
+    const float lse = empty ? kNegInf : m_run * p.scale + __logf(l_tot);
+    p.lse[it.b * p.lse_sb + it.h * p.lse_sh + qi] = lse;
+  }
+}
+
+// ------------------------------------------------------------------ f32 path
+
+// LDS row stride (floats) of the fp32 tiles: padded against bank conflicts.
+constexpr int kF32Row = kD + 4;
+
+template <int WAVES, bool SPARSE>
+__global__ __launch_bounds__(WAVES * 64) void attn_fwd_f32_kernel(AttnParams p) {
+  constexpr int NT = WAVES * 64;
+  constexpr int BM = WAVES * kQW;
+  static_assert(!SPARSE || BM == kMaskBlock, "sparse kernel works on one mask row");
+
+  __shared__ __attribute__((aligned(16))) float lds_k[kBN * kF32Row];
+  __shared__ __attribute__((aligned(16))) float lds_v[kBN * kF32Row];
+  extern __shared__ unsigned short kept_dyn[];
+  __shared__ int wave_cnt[WAVES];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  int item;
+  if constexpr (SPARSE) {
+    item = p.order ? p.order[blockIdx.x] : (int)blockIdx.x;
+  } else {
+    item = xcd_remap(blockIdx.x, gridDim.x);
+  }
+  const Item it = decode_item(item, p.n_qblk, p.H);
+  const int qi = it.qblk * BM + wave * kQW + l32;
+  const bool q_ok = qi < p.Sq;
+
+  const float* qp = static_cast<const float*>(p.q) + it.b * p.q_sb + it.h * p.q_sh;
+  const float* kp = static_cast<const float*>(p.k) + it.b * p.k_sb + it.h * p.k_sh;
+  const float* vp = static_cast<const float*>(p.v) + it.b * p.v_sb + it.h * p.v_sh;
+
+  int n_tiles;
+  const unsigned short* kept = kept_dyn;
+  if constexpr (SPARSE) {
+    const uint8_t* mrow = p.mask + (((int64_t)it.b * p.H + it.h) * p.n_mqb + it.qblk) * p.n_mkb;
+    n_tiles = 2 * build_kept_list<NT>(mrow, p.n_mkb, kept_dyn, wave_cnt);
+  } else {
+    n_tiles = (p.Skv + kBN - 1) / kBN;
+  }
+
+  // Q: lane holds Q[qi][2 s + hh], s = 0..63
+  float qf[64];
+#pragma unroll
+  for (int s = 0; s < 64; ++s) qf[s] = q_ok ? qp[(int64_t)qi * p.q_ss + 2 * s + hh] : 0.0f;
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+  float m_run = kNegInf, l_run = 0.0f;
+  const float c = p.scale_log2;
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int key0 = tile_key0<SPARSE>(t, kept);
+    // stage the tile: 64 rows x 32 float4 chunks per tensor
+    for (int cid = tid; cid < kBN * (kD / 4); cid += NT) {
+      const int row = cid >> 5, ch = cid & 31;
+      const int key = key0 + row;
+      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+      if (key < p.Skv) {
+        kv = *reinterpret_cast<const f32x4*>(kp + (int64_t)key * p.k_ss + ch * 4);
+        vv = *reinterpret_cast<const f32x4*>(vp + (int64_t)key * p.v_ss + ch * 4);
+      }
+      *reinterpret_cast<f32x4*>(&lds_k[row * kF32Row + ch * 4]) = kv;
+      *reinterpret_cast<f32x4*>(&lds_v[row * kF32Row + ch * 4]) = vv;
+    }
+    __syncthreads();
+
+    f32x16 st[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[kb][r] = 0.0f;
+      const int row = kb * 32 + l32;
+#pragma unroll
+      for (int s = 0; s < 64; ++s)
+        st[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(lds_k[row * kF32Row + 2 * s + hh], qf[s],
+                                                      st[kb], 0, 0, 0);
+    }
+    if (key0 + kBN > p.Skv) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key >= p.Skv) st[kb][r] = kNegInf;
+        }
+    }
+    float mx = st[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
+    mx = pair_max(mx);
+    const bool need = (mx - m_run) * c > kRescaleLog2;
+    if (wave_any(need)) {
+      const float m_new = need ? mx : m_run;
+      const float alpha = need ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.0f;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float mc = (m_run == kNegInf) ? 0.0f : m_run * c;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][r], c, -mc));
+        l_run += e;
+        st[kb][r] = e;
+      }
+    // O^T += V^T P^T, one key per MFMA step: half hh uses key
+    // kb*32 + 8 (r/4) + 4 hh + r%4, the key its register r holds.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(lds_v[row * kF32Row + db * 32 + l32],
+                                                         st[kb][r], acc[db], 0, 0, 0);
+      }
+    __syncthreads();
+  }
+
+  const float l_tot = pair_sum(l_run);
+  if (!q_ok) return;
+  float* op = p.o + it.b * p.o_sb + it.h * p.o_sh + (int64_t)qi * p.o_ss;
+  const bool empty = !(l_tot > 0.0f);
+  const float inv_l = empty ? 0.0f : 1.0f / l_tot;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = db * 32 + 8 * g4 + 4 * hh;
+      f32x4 o4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o4[i] = acc[db][4 * g4 + i] * inv_l;
+      *reinterpret_cast<f32x4*>(op + d) = o4;
+    }
+  if (hh == 0) {
+    const float lse = empty ? kNegInf : m_run * p.scale + __logf(l_tot);
+    p.lse[it.b * p.lse_sb + it.h * p.lse_sh + qi] = lse;
+  }
+}
+
+// O = 0, LSE = -inf for every row (attention over an empty key set).
+__global__ void attn_empty_kernel(AttnParams p) {
+  const int64_t rows = (int64_t)p.B * p.Sq * p.H;
+  for (int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; r < rows;
+       r += (int64_t)gridDim.x * blockDim.x) {
+    const int h = (int)(r % p.H);
+    const int64_t bs = r / p.H;
+    const int s = (int)(bs % p.Sq);
+    const int b = (int)(bs / p.Sq);
+    float* op = p.o + b * p.o_sb + h * p.o_sh + (int64_t)s * p.o_ss;
+    for (int d = 0; d < kD; d += 4) *reinterpret_cast<f32x4*>(op + d) = f32x4{0.f, 0.f, 0.f, 0.f};
+    p.lse[b * p.lse_sb + h * p.lse_sh + s] = kNegInf;
+  }
+}
+
+int env_int(const char* name, int dflt) {
+  const char* s = std::getenv(name);
+  if (!s || !*s) return dflt;
+  return std::atoi(s);
+}
+
+}  // namespace
+
+int dense_rows_per_block(DType dt, int64_t Sq) {
+  (void)Sq;
+  if (dt == DType::F32) return 4 * kQW;
+  static const int waves = env_int("LSH_DENSE_WAVES", 8);
+  return (waves == 4 ? 4 : 8) * kQW;
+}
+
+hipError_t launch_attn_dense(const AttnParams& p0, DType dt, hipStream_t s) {
+  AttnParams p = p0;
+  if (dt == DType::F32) {
+    p.n_qblk = (p.Sq + 127) / 128;
+    p.n_items = p.B * p.H * p.n_qblk;
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<4, false>), dim3(p.n_items), dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
+  int waves = dense_rows_per_block(dt, p.Sq) / kQW;
+  // Small grids: 4-wave workgroups spread better over 256 CUs. Per-query
+  // arithmetic is identical for either size.
+  const int64_t items8 = (int64_t)p.B * p.H * ((p.Sq + 255) / 256);
+  if (waves == 8 && items8 < 512 && env_int("LSH_DENSE_WAVES", 0) == 0) waves = 4;
+  const int bm = waves * kQW;
+  p.n_qblk = (p.Sq + bm - 1) / bm;
+  p.n_items = p.B * p.H * p.n_qblk;
+  if (waves == 8)
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<8, false>), dim3(p.n_items), dim3(512), 0, s, p);
+  else
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<4, false>), dim3(p.n_items), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_sparse(const AttnParams& p0, DType dt, hipStream_t s) {
+  AttnParams p = p0;
+  p.n_qblk = p.n_mqb;
+  p.n_items = p.B * p.H * p.n_mqb;
+  const size_t dyn = sizeof(unsigned short) * (size_t)p.n_mkb;
+  if (dt == DType::F32)
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<4, true>), dim3(p.n_items), dim3(256), dyn, s, p);
+  else
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<4, true>), dim3(p.n_items), dim3(256), dyn, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_empty(const AttnParams& p, hipStream_t s) {
+  const int64_t rows = (int64_t)p.B * p.Sq * p.H;
+  int64_t blocks = (rows + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(attn_empty_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace lsh

@@ -1,0 +1,59 @@
+// Internal declarations shared by the liblsh translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lsh {
+
+// Key tile of the attention kernels (keys per online-softmax step).
+constexpr int kBN = 64;
+// Head dimension supported by the kernels.
+constexpr int kD = 128;
+// Query rows per wavefront (one 32x32 MFMA block).
+constexpr int kQW = 32;
+// Mask block edge of the block-sparse kernel.
+constexpr int kMaskBlock = 128;
+
+// Kernel-side description of one attention launch. Strides are in
+// elements. LSE of (b, h, s) lives at lse[b * lse_sb + h * lse_sh + s].
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o;
+  float* lse;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int64_t lse_sb, lse_sh;
+  int32_t B, H, Sq, Skv;
+  float scale;        // score multiplier
+  float scale_log2;   // scale * log2(e)
+  int32_t n_qblk;     // query blocks per (b, h)
+  int32_t n_items;    // grid size in work items
+  // block-sparse only
+  const uint8_t* mask;      // [B, H, n_mqb, n_mkb]
+  int32_t n_mqb, n_mkb;
+  const int32_t* order;     // work order over items, or nullptr
+};
+
+enum class DType : int { F32 = 0, BF16 = 1 };
+
+// Launchers (return the launch's hipError_t).
+hipError_t launch_attn_dense(const AttnParams& p, DType dt, hipStream_t s);
+hipError_t launch_attn_sparse(const AttnParams& p, DType dt, hipStream_t s);
+hipError_t launch_attn_empty(const AttnParams& p, hipStream_t s);
+hipError_t launch_head_permute(const void* src, void* dst, int elem_bytes,
+                               int64_t B, int64_t S, int64_t H, int64_t D,
+                               int32_t h0, int32_t hc, hipStream_t s);
+hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, int32_t n,
+                            int64_t B, int64_t Sq, int64_t H, float* o, float* lse,
+                            hipStream_t s);
+hipError_t launch_sparse_schedule(const uint8_t* mask, int32_t n_items, int32_t n_mkb,
+                                  int32_t* counts, int32_t* order, hipStream_t s);
+
+// Query rows per workgroup of the dense kernel for a given query length.
+int dense_rows_per_block(DType dt, int64_t Sq);
+
+}  // namespace lsh

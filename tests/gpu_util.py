@@ -1,0 +1,74 @@
+"""Helpers of the GPU parity tests: upload seeded inputs, NaN-poisoned
+outputs, error measures. Tolerances of the HIP path against the fp64
+oracle (max |difference| over all elements; any NaN or Inf fails):
+  O: <= 1e-4 for float32 inputs, <= 2e-2 for bfloat16 inputs (N(0,1) data)
+  LSE: <= 1e-3
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+TOL_O = {"f32": 1e-4, "bf16": 2e-2}
+TOL_LSE = 1e-3
+
+
+def torch():
+    import torch as t
+    return t
+
+
+def to_gpu(tensor, dtype: str):
+    """lsh_inputs.Tensor -> GPU tensor with exactly the values the oracle sees."""
+    t = torch()
+    if dtype == "bf16":
+        return t.from_numpy(np.ascontiguousarray(tensor.bits).view(np.int16)).view(t.bfloat16).cuda()
+    return t.from_numpy(np.ascontiguousarray(tensor.values)).cuda()
+
+
+def values_to_gpu(values: np.ndarray, dtype: str):
+    """float array whose values are already representable in `dtype`."""
+    t = torch()
+    x = t.from_numpy(np.ascontiguousarray(values, dtype=np.float32))
+    if dtype == "bf16":
+        y = x.to(t.bfloat16)
+        assert t.equal(y.float(), x), "values not exactly representable in bf16"
+        return y.cuda()
+    return x.cuda()
+
+
+def poisoned_outputs(B, Sq, H, D=128):
+    t = torch()
+    o = t.full((B, Sq, H, D), float("nan"), dtype=t.float32, device="cuda")
+    lse = t.full((B, H, Sq), float("nan"), dtype=t.float32, device="cuda")
+    return o, lse
+
+
+def max_err(got, want) -> float:
+    """max |got - want| in float64; inf if any NaN, or if infinities disagree."""
+    g = np.asarray(got, dtype=np.float64)
+    w = np.asarray(want, dtype=np.float64)
+    assert g.shape == w.shape, (g.shape, w.shape)
+    if np.isnan(g).any() or np.isnan(w).any():
+        return float("inf")
+    same_inf = np.isinf(g) & np.isinf(w) & (np.sign(g) == np.sign(w))
+    if (np.isinf(g) ^ np.isinf(w)).any():
+        return float("inf")
+    with np.errstate(invalid="ignore"):
+        d = np.where(same_inf, 0.0, np.abs(g - w))
+    return float(d.max()) if d.size else 0.0
+
+
+def check(name, dtype, o_got, lse_got, o_ref, lse_ref, tol_o=None, tol_lse=TOL_LSE):
+    eo = max_err(o_got, o_ref)
+    el = max_err(lse_got, lse_ref)
+    print(f"[parity] {name}: max|dO|={eo:.3e} max|dLSE|={el:.3e}", file=sys.stderr, flush=True)
+    tol_o = TOL_O[dtype] if tol_o is None else tol_o
+    assert eo <= tol_o, f"{name}: O error {eo} > {tol_o}"
+    assert el <= tol_lse, f"{name}: LSE error {el} > {tol_lse}"
+    return eo, el
+
+
+def announce(msg):
+    print(f"[case] {msg}", file=sys.stderr, flush=True)

@@ -1,0 +1,284 @@
+"""HIP path vs the fp64 oracle on small and odd shapes, closed forms on the
+GPU, strided inputs, peaked and monotone score patterns (lazy-rescale
+paths), and determinism. Sizes keep the oracle to seconds while spanning
+several 64-key tiles, several query blocks and ragged tails."""
+import math
+
+import numpy as np
+import pytest
+
+import lsh_inputs as I
+import oracle
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    import long_sequence_head_amd as lsh
+    lsh.load()
+    return lsh
+
+
+SHAPES = [  # (B, Sq, Skv, H)
+    (1, 1, 1, 1), (1, 2, 3, 2), (1, 63, 64, 1), (1, 64, 65, 2), (2, 127, 128, 2),
+    (1, 128, 129, 3), (1, 200, 255, 2), (1, 257, 256, 2), (2, 300, 1000, 3),
+    (1, 1000, 1000, 4), (1, 513, 77, 2),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_dense_vs_oracle(L, dtype, shape):
+    B, Sq, Skv, H = shape
+    G.announce(f"dense {dtype} B={B} Sq={Sq} Skv={Skv} H={H}")
+    q, k, v = I.make_custom((B, Sq, H, 128), (B, Skv, H, 128), dtype, seed=Sq * 7 + Skv)
+    o, lse = G.poisoned_outputs(B, Sq, H)
+    L.attn_fwd(G.to_gpu(q, dtype), G.to_gpu(k, dtype), G.to_gpu(v, dtype), o=o, lse=lse)
+    o_ref, lse_ref = oracle.attention_ref(q.values, k.values, v.values, 1 / math.sqrt(128))
+    G.check(f"dense {dtype} {shape}", dtype, o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_closed_forms_on_gpu(L, dtype):
+    """constant V -> O = c; identical keys -> O = mean V and
+    LSE = scale <q, kappa> + ln Skv; one key -> O = v_0."""
+    G.announce(f"closed forms {dtype}")
+    t = G.torch()
+    B, Sq, Skv, H, D = 1, 130, 333, 2, 128
+    q, k, v = I.make_custom((B, Sq, H, D), (B, Skv, H, D), dtype, seed=5)
+    scale = 1 / math.sqrt(D)
+    # constant V (values exactly representable: multiples of 1/8)
+    c = (np.arange(D) % 17 - 8) / 8.0
+    vc = np.broadcast_to(c, (B, Skv, H, D)).astype(np.float32)
+    o, lse = G.poisoned_outputs(B, Sq, H)
+    L.attn_fwd(G.to_gpu(q, dtype), G.to_gpu(k, dtype), G.values_to_gpu(vc, dtype), o=o, lse=lse)
+    err = G.max_err(o.cpu().numpy(), np.broadcast_to(c, (B, Sq, H, D)))
+    # fp32: weights summing to one up to fp32 rounding; bf16: P is rounded
+    # to bf16 in the numerator (relative 2^-9) but not in the row sum
+    assert err <= (1e-5 if dtype == "f32" else 2e-3), err
+    # identical keys
+    kappa = np.round(np.linspace(-1, 1, D) * 8) / 8
+    kc = np.broadcast_to(kappa, (B, Skv, H, D)).astype(np.float32)
+    o, lse = G.poisoned_outputs(B, Sq, H)
+    L.attn_fwd(G.to_gpu(q, dtype), G.values_to_gpu(kc, dtype), G.to_gpu(v, dtype), o=o, lse=lse)
+    mean_v = v.values.astype(np.float64).mean(axis=1, keepdims=True)
+    eo = G.max_err(o.cpu().numpy(), np.broadcast_to(mean_v, (B, Sq, H, D)))
+    want_lse = scale * np.einsum("bshd,d->bhs", q.values.astype(np.float64), kappa) + math.log(Skv)
+    el = G.max_err(lse.cpu().numpy(), want_lse)
+    assert eo <= G.TOL_O[dtype] and el <= G.TOL_LSE, (eo, el)
+    # single key
+    o, lse = G.poisoned_outputs(B, Sq, H)
+    kt, vt = G.to_gpu(k, dtype)[:, :1], G.to_gpu(v, dtype)[:, :1]
+    L.attn_fwd(G.to_gpu(q, dtype), kt, vt, o=o, lse=lse)
+    eo = G.max_err(o.cpu().numpy(), np.broadcast_to(v.values[:, :1], (B, Sq, H, D)))
+    # exp2(fma(s, c, -m c)) of the single key is 1 up to the rounding of m c
+    assert eo <= 1e-6, eo
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_strided_packed_qkv(L, dtype):
+    """Q, K, V as views into one packed [B, S, 3, H, D] buffer; O written
+    into a view of a wider buffer."""
+    G.announce(f"strided {dtype}")
+    t = G.torch()
+    B, S, H, D = 2, 333, 3, 128
+    q, k, v = I.make_custom((B, S, H, D), (B, S, H, D), dtype, seed=11)
+    packed = t.stack([G.to_gpu(q, dtype), G.to_gpu(k, dtype), G.to_gpu(v, dtype)], dim=2)
+    qv, kv, vv = packed[:, :, 0], packed[:, :, 1], packed[:, :, 2]
+    wide = t.full((B, S, H + 2, D), float("nan"), dtype=t.float32, device="cuda")
+    o = wide[:, :, 1:H + 1]
+    lse = t.full((B, H, S), float("nan"), dtype=t.float32, device="cuda")
+    L.attn_fwd(qv, kv, vv, o=o, lse=lse)
+    o_ref, lse_ref = oracle.attention_ref(q.values, k.values, v.values, 1 / math.sqrt(D))
+    G.check(f"strided {dtype}", dtype, o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+    assert t.isnan(wide[:, :, 0]).all() and t.isnan(wide[:, :, H + 1]).all(), "wrote outside O"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_peaked_scores(L, dtype):
+    """Q scaled by 8: softmax dominated by few keys."""
+    G.announce(f"peaked {dtype}")
+    B, Sq, Skv, H, D = 1, 260, 700, 2, 128
+    q, k, v = I.make_custom((B, Sq, H, D), (B, Skv, H, D), dtype, seed=21)
+    qv = q.values * 8.0   # exact in bf16 (power of two)
+    o, lse = G.poisoned_outputs(B, Sq, H)
+    L.attn_fwd(G.values_to_gpu(qv, dtype), G.to_gpu(k, dtype), G.to_gpu(v, dtype), o=o, lse=lse)
+    o_ref, lse_ref = oracle.attention_ref(qv, k.values, v.values, 1 / math.sqrt(D))
+    G.check(f"peaked {dtype}", dtype, o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("direction", [1, -1])
+def test_monotone_scores(L, dtype, direction):
+    """Scores that rise (or fall) along the keys by ~64 raw units per 64-key
+    tile: with direction=1 the running max moves on every tile."""
+    G.announce(f"monotone {dtype} {direction}")
+    B, Sq, Skv, H, D = 1, 70, 900, 2, 128
+    q = np.zeros((B, Sq, H, D), np.float32)
+    q[..., 0] = 8.0
+    q[..., 1] = np.linspace(-1, 1, Sq, dtype=np.float32)[None, :, None]
+    k = np.zeros((B, Skv, H, D), np.float32)
+    k[..., 0] = direction * np.arange(Skv, dtype=np.float32)[None, :, None] / 8.0
+    k[..., 1] = 1.0
+    k = k.astype(np.float32)
+    if dtype == "bf16":
+        import lsh_inputs as II
+        k = II.bf16_bits_to_f32(II.bf16_bits(k))
+        q = II.bf16_bits_to_f32(II.bf16_bits(q))
+    _, _, v = I.make_custom((B, Sq, H, D), (B, Skv, H, D), dtype, seed=31)
+    o, lse = G.poisoned_outputs(B, Sq, H)
+    L.attn_fwd(G.values_to_gpu(q, dtype), G.values_to_gpu(k, dtype), G.to_gpu(v, dtype), o=o, lse=lse)
+    o_ref, lse_ref = oracle.attention_ref(q, k, v.values, 1 / math.sqrt(D))
+    G.check(f"monotone {dtype} {direction}", dtype, o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+
+
+def test_run_to_run_bit_identical(L):
+    G.announce("run-to-run")
+    t = G.torch()
+    q, k, v = I.make_custom((1, 1500, 4, 128), (1, 1500, 4, 128), "bf16", seed=41)
+    qg, kg, vg = G.to_gpu(q, "bf16"), G.to_gpu(k, "bf16"), G.to_gpu(v, "bf16")
+    o1, l1 = L.attn_fwd(qg, kg, vg)
+    for _ in range(3):
+        o2, l2 = L.attn_fwd(qg, kg, vg)
+        assert t.equal(o1, o2) and t.equal(l1, l2)
+
+
+def test_workgroup_size_does_not_change_bits(L):
+    """Head 0 alone launches 4-wave workgroups, all 8 heads launch 8-wave
+    ones; chunking {1, 7} vs unchunked compares the two bit for bit."""
+    G.announce("workgroup-size invariance")
+    t = G.torch()
+    S, H = 16384, 8
+    q, k, v = I.make_custom((1, S, H, 128), (1, S, H, 128), "bf16", seed=43)
+    qg, kg, vg = G.to_gpu(q, "bf16"), G.to_gpu(k, "bf16"), G.to_gpu(v, "bf16")
+    o1, l1 = L.attn_fwd(qg, kg, vg)
+    o2, l2 = L.attn_fwd_chunked(qg, kg, vg, [1, 7])
+    t.cuda.synchronize()
+    assert t.equal(o1, o2) and t.equal(l1, l2)
+    o3, l3 = L.attn_fwd(qg[:, :, :1].contiguous(), kg[:, :, :1].contiguous(), vg[:, :, :1].contiguous())
+    assert t.equal(o1[:, :, :1], o3) and t.equal(l1[:, :1], l3)
+
+
+def test_permute_bit_exact(L):
+    G.announce("permute")
+    t = G.torch()
+    for dtype, shape in [("bf16", (2, 333, 5, 128)), ("f32", (1, 200, 7, 128)), ("bf16", (1, 70, 3, 64))]:
+        x = I.make_tensor(shape, dtype, 77, 0, seed=1)
+        xg = G.to_gpu(x, dtype)
+        H = shape[2]
+        for h0, hc in [(0, H), (1, H - 1), (H - 1, 1)]:
+            y = L.head_permute(xg, h0, hc)
+            want = oracle.permute_ref(x.device_array, h0, hc)
+            got = y.cpu()
+            got = got.view(t.int16).numpy().view(np.uint16) if dtype == "bf16" else got.numpy()
+            assert np.array_equal(got, want), (dtype, shape, h0, hc)
+
+
+def test_chunked_small_bit_identical(L):
+    G.announce("chunked small")
+    t = G.torch()
+    B, S, H = 2, 777, 7
+    q, k, v = I.make_custom((B, S, H, 128), (B, S, H, 128), "bf16", seed=51)
+    qg, kg, vg = G.to_gpu(q, "bf16"), G.to_gpu(k, "bf16"), G.to_gpu(v, "bf16")
+    o1, l1 = L.attn_fwd(qg, kg, vg)
+    for chunks in ([7], [3, 4], [1, 1, 5], [2, 2, 2, 1]):
+        o2, l2 = G.poisoned_outputs(B, S, H)
+        L.attn_fwd_chunked(qg, kg, vg, chunks, o=o2, lse=l2)
+        t.cuda.synchronize()
+        assert t.equal(o1, o2) and t.equal(l1, l2), chunks
+    # same stream for both roles
+    o3, l3 = G.poisoned_outputs(B, S, H)
+    s = t.cuda.current_stream()
+    L.attn_fwd_chunked(qg, kg, vg, [3, 4], o=o3, lse=l3, compute_stream=s, permute_stream=s)
+    assert t.equal(o1, o3) and t.equal(l1, l3)
+    o_ref, lse_ref = oracle.attention_ref(q.values, k.values, v.values, 1 / math.sqrt(128))
+    G.check("chunked small", "bf16", o1.cpu().numpy(), l1.cpu().numpy(), o_ref, lse_ref)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_partial_and_merge_small(L, dtype):
+    """Uneven KV split incl. an empty block; GPU partials + GPU merge vs the
+    oracle's full attention, and the GPU merge vs the oracle merge of the
+    same partials."""
+    G.announce(f"partial+merge {dtype}")
+    t = G.torch()
+    B, Sq, Skv, H = 1, 300, 1000, 3
+    q, k, v = I.make_custom((B, Sq, H, 128), (B, Skv, H, 128), dtype, seed=61)
+    qg, kg, vg = G.to_gpu(q, dtype), G.to_gpu(k, dtype), G.to_gpu(v, dtype)
+    cuts = [0, 1, 64, 64, 500, 1000]
+    n = len(cuts) - 1
+    o_parts = t.full((n, B, Sq, H, 128), float("nan"), dtype=t.float32, device="cuda")
+    l_parts = t.full((n, B, H, Sq), float("nan"), dtype=t.float32, device="cuda")
+    for i, (a, b) in enumerate(zip(cuts[:-1], cuts[1:])):
+        L.attn_partial(qg, kg[:, a:b], vg[:, a:b], o=o_parts[i], lse=l_parts[i])
+    assert t.isneginf(l_parts[2]).all() and (o_parts[2] == 0).all(), "empty block"
+    o, lse = L.lse_merge(o_parts, l_parts)
+    o_ref, lse_ref = oracle.attention_ref(q.values, k.values, v.values, 1 / math.sqrt(128))
+    G.check(f"merge-vs-full {dtype}", dtype, o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+    om, lm = oracle.merge_ref(o_parts.cpu().numpy(), l_parts.cpu().numpy())
+    G.check(f"merge-vs-oracle-merge {dtype}", dtype, o.cpu().numpy(), lse.cpu().numpy(), om, lm,
+            tol_o=1e-5, tol_lse=1e-5)
+
+
+def test_merge_all_empty(L):
+    G.announce("merge all empty")
+    t = G.torch()
+    o_parts = t.zeros((3, 1, 5, 2, 128), dtype=t.float32, device="cuda")
+    l_parts = t.full((3, 1, 2, 5), float("-inf"), dtype=t.float32, device="cuda")
+    o, lse = L.lse_merge(o_parts, l_parts)
+    assert (o == 0).all() and t.isneginf(lse).all()
+
+
+SPARSE_CASES = [  # (Sq, Skv, H)
+    (128, 128, 1), (300, 257, 2), (640, 1000, 2), (1024, 1024, 3),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", SPARSE_CASES, ids=lambda s: "x".join(map(str, s)))
+def test_blocksparse_vs_oracle(L, dtype, case):
+    Sq, Skv, H = case
+    G.announce(f"sparse {dtype} {case}")
+    t = G.torch()
+    q, k, v = I.make_custom((1, Sq, H, 128), (1, Skv, H, 128), dtype, seed=Sq + Skv)
+    nqb, nkb = -(-Sq // 128), -(-Skv // 128)
+    rng = np.random.default_rng(Sq * 31 + Skv)
+    mask = (rng.random((1, H, nqb, nkb)) < 0.4).astype(np.uint8)
+    mask[0, 0, 0, :] = 0          # a query block with no kept key block
+    if nkb > 1:
+        mask[0, -1, -1, :] = 0
+        mask[0, -1, -1, nkb - 1] = 1   # only the partial last key block
+    o, lse = G.poisoned_outputs(1, Sq, H)
+    L.attn_fwd_blocksparse(G.to_gpu(q, dtype), G.to_gpu(k, dtype), G.to_gpu(v, dtype),
+                           t.from_numpy(mask).cuda(), o=o, lse=lse)
+    o_ref, lse_ref = oracle.attention_ref(q.values, k.values, v.values, 1 / math.sqrt(128),
+                                          block_mask=mask)
+    G.check(f"sparse {dtype} {case}", dtype, o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+
+
+def test_blocksparse_all_ones_equals_dense_bitwise(L):
+    G.announce("sparse all-ones")
+    t = G.torch()
+    Sq, Skv, H = 700, 650, 3
+    q, k, v = I.make_custom((1, Sq, H, 128), (1, Skv, H, 128), "bf16", seed=91)
+    qg, kg, vg = G.to_gpu(q, "bf16"), G.to_gpu(k, "bf16"), G.to_gpu(v, "bf16")
+    mask = t.ones((1, H, 6, 6), dtype=t.uint8, device="cuda")
+    o1, l1 = L.attn_fwd_blocksparse(qg, kg, vg, mask)
+    o2, l2 = L.attn_fwd(qg, kg, vg)
+    assert t.equal(o1, o2) and t.equal(l1, l2)
+
+
+def test_blocksparse_diagonal_is_blockwise_dense(L):
+    G.announce("sparse diagonal")
+    t = G.torch()
+    S, H = 640, 2
+    q, k, v = I.make_custom((1, S, H, 128), (1, S, H, 128), "bf16", seed=93)
+    qg, kg, vg = G.to_gpu(q, "bf16"), G.to_gpu(k, "bf16"), G.to_gpu(v, "bf16")
+    mask = t.eye(5, dtype=t.uint8, device="cuda").expand(1, H, 5, 5).contiguous()
+    o1, l1 = L.attn_fwd_blocksparse(qg, kg, vg, mask)
+    for i in range(5):
+        sl = slice(128 * i, 128 * (i + 1))
+        o2, l2 = L.attn_fwd(qg[:, sl], kg[:, sl], vg[:, sl])
+        assert t.equal(o1[:, sl], o2) and t.equal(l1[:, :, sl], l2), i
