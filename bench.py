@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""Attention forward throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads 4,3,2,5]
+
+Headline (the JSON line's `value`): dense non-causal bf16 attention,
+B=1, S=56160, H=40, D=128, fp32 O + LSE, algorithmic TFLOP/s =
+4*B*H*S*S*D / time. One step = one lsh_attn_fwd over the whole input.
+Secondary workloads (same line, under "workloads"): the head-chunked
+two-stream pipeline at S=32760 ({16,12,12} chunks, permute included), the
+ring partials + LSE merge (Q 4096 tokens, 8 KV blocks of 4096, H=8) and
+the block-sparse workload (S=32768, 128x128 mask, per-head density
+U[0.1,0.6)). Inputs are the seeded synthetic tensors of lsh_inputs,
+resident in HBM before timing. `cpu_baseline` times the fp64 oracle on a
+bounded sample of the headline workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s and % bf16 MFMA peak at S=32K/56K, 1 MI355X"
+PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_S56160_H40_traffic.json")
+KERNEL_SOURCES = ["long_sequence_head_amd/csrc/attn_fwd.hip",
+                  "long_sequence_head_amd/csrc/lsh_internal.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def upload(t, dtype):
+    import numpy as np
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(t.values)).cuda()
+
+
+def timed(fn, steps, warmup):
+    """ms per call of fn over `steps` calls after `warmup` calls, measured
+    with events on the current stream between two device synchronisations."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - w0) * 1e3 / steps
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def flush_l2_mall(buf):
+    buf.fill_(1.0)   # 512 MiB write evicts L2 and the 256 MiB Infinity Cache
+
+
+# ------------------------------------------------------------------ workloads
+
+def bench_dense(L, I, w, steps, warmup):
+    import torch
+    log(f"[bench] workload {w.wid}: {w.name}: generating inputs")
+    q, k, v = I.make_qkv(w, seed=0)
+    qg, kg, vg = upload(q, w.dtype), upload(k, w.dtype), upload(v, w.dtype)
+    o = torch.empty((w.B, w.Sq, w.H, w.D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device="cuda")
+    ms, wall = timed(lambda: L.attn_fwd(qg, kg, vg, o=o, lse=lse), steps, warmup)
+    flops = 4 * w.B * w.H * w.Sq * w.Skv * w.D
+    tf = flops / ms / 1e9
+    log(f"[bench] workload {w.wid}: {ms:.3f} ms/step, {tf:.1f} TFLOP/s ({100 * tf / PEAK_BF16_TFLOPS:.1f}% of peak)")
+    return dict(ms=ms, wall_ms=wall, tflops=tf, flops=flops), (q, k, v, o, lse)
+
+
+def bench_chunked(L, I, w, steps, warmup):
+    import torch
+    log(f"[bench] workload {w.wid}: {w.name}: generating inputs")
+    q, k, v = I.make_qkv(w, seed=0)
+    qg, kg, vg = upload(q, w.dtype), upload(k, w.dtype), upload(v, w.dtype)
+    del q, k, v
+    o = torch.empty((w.B, w.Sq, w.H, w.D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(L.chunked_workspace_bytes(qg, kg, vg) + 256, dtype=torch.uint8, device="cuda")
+    chunks = list(w.head_chunks)
+    ms_pipe, _ = timed(lambda: L.attn_fwd_chunked(qg, kg, vg, chunks, o=o, lse=lse, workspace=ws),
+                       steps, warmup)
+    ms_attn, _ = timed(lambda: L.attn_fwd(qg, kg, vg, o=o, lse=lse), steps, warmup)
+    perm = torch.empty((w.B, w.H, w.Sq, w.D), dtype=qg.dtype, device="cuda")
+
+    def permute_all():
+        for x in (qg, kg, vg):
+            L.head_permute(x, 0, w.H, out=perm)
+    ms_perm, _ = timed(permute_all, steps, warmup)
+    flops = 4 * w.B * w.H * w.Sq * w.Skv * w.D
+    perm_bytes = 3 * 2 * qg.numel() * qg.element_size()
+    r = dict(pipeline_ms=ms_pipe, pipeline_tflops=flops / ms_pipe / 1e9,
+             unchunked_attn_ms=ms_attn, unchunked_attn_tflops=flops / ms_attn / 1e9,
+             permute_qkv_ms=ms_perm, permute_GBs=perm_bytes / ms_perm / 1e6,
+             chunks=chunks)
+    log(f"[bench] workload {w.wid}: pipeline {ms_pipe:.3f} ms ({r['pipeline_tflops']:.1f} TFLOP/s), "
+        f"unchunked {ms_attn:.3f} ms, permute Q+K+V {ms_perm:.3f} ms ({r['permute_GBs']:.0f} GB/s)")
+    return r
+
+
+def bench_ring(L, I, w, steps, warmup):
+    import torch
+    log(f"[bench] workload {w.wid}: {w.name}: generating inputs")
+    q, k, v = I.make_qkv(w, seed=0)
+    qg, kg, vg = upload(q, w.dtype), upload(k, w.dtype), upload(v, w.dtype)
+    del q, k, v
+    n, blk = w.kv_blocks, w.Skv // w.kv_blocks
+    o_parts = torch.empty((n, w.B, w.Sq, w.H, w.D), dtype=torch.float32, device="cuda")
+    l_parts = torch.empty((n, w.B, w.H, w.Sq), dtype=torch.float32, device="cuda")
+    o = torch.empty((w.B, w.Sq, w.H, w.D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device="cuda")
+    kb = [kg[:, i * blk:(i + 1) * blk] for i in range(n)]
+    vb = [vg[:, i * blk:(i + 1) * blk] for i in range(n)]
+
+    def partials():
+        for i in range(n):
+            L.attn_partial(qg, kb[i], vb[i], o=o_parts[i], lse=l_parts[i])
+
+    def step():
+        partials()
+        L.lse_merge(o_parts, l_parts, o=o, lse=lse)
+    ms_step, _ = timed(step, steps, warmup)
+    ms_part, _ = timed(partials, steps, warmup)
+    # merge from HBM: flush L2 and the Infinity Cache before each timed call
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    times = []
+    for i in range(warmup + steps):
+        flush_l2_mall(flush)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        L.lse_merge(o_parts, l_parts, o=o, lse=lse)
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= warmup:
+            times.append(e0.elapsed_time(e1))
+    ms_merge = sum(times) / len(times)
+    flops = 4 * w.B * w.H * w.Sq * w.Skv * w.D
+    mbytes = (o_parts.numel() + l_parts.numel() + o.numel() + lse.numel()) * 4
+    r = dict(step_ms=ms_step, partials_ms=ms_part, partials_tflops=flops / ms_part / 1e9,
+             merge_ms=ms_merge, merge_GBs=mbytes / ms_merge / 1e6, merge_bytes=mbytes)
+    log(f"[bench] workload {w.wid}: step {ms_step:.3f} ms, 8 partials {ms_part:.3f} ms "
+        f"({r['partials_tflops']:.1f} TFLOP/s), merge {ms_merge * 1e3:.1f} us ({r['merge_GBs']:.0f} GB/s)")
+    return r
+
+
+def bench_sparse(L, I, w, steps, warmup):
+    import torch
+    log(f"[bench] workload {w.wid}: {w.name}: generating inputs")
+    q, k, v = I.make_qkv(w, seed=0)
+    qg, kg, vg = upload(q, w.dtype), upload(k, w.dtype), upload(v, w.dtype)
+    del q, k, v
+    nb = w.Sq // I.MASK_BLOCK
+    mask, dens = I.make_block_mask(w.B, w.H, nb, nb, seed=0)
+    mg = torch.from_numpy(mask).cuda()
+    o = torch.empty((w.B, w.Sq, w.H, w.D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(L.blocksparse_workspace_bytes(qg, kg, vg) + 256, dtype=torch.uint8, device="cuda")
+    ms, _ = timed(lambda: L.attn_fwd_blocksparse(qg, kg, vg, mg, o=o, lse=lse, workspace=ws),
+                  steps, warmup)
+    nnz = int(mask.astype(bool).sum())
+    flops = nnz * 4 * I.MASK_BLOCK * I.MASK_BLOCK * w.D
+    r = dict(ms=ms, tflops=flops / ms / 1e9, kept_blocks=nnz, kept_flops=flops,
+             density_mean=float(dens.mean()), density_min=float(dens.min()),
+             density_max=float(dens.max()))
+    log(f"[bench] workload {w.wid}: {ms:.3f} ms, {r['tflops']:.1f} TFLOP/s on kept blocks "
+        f"(mean density {r['density_mean']:.3f})")
+    return r
+
+
+# ---------------------------------------------------------------- CPU oracle
+
+def cpu_baseline(I, w, q, k, v, o_gpu, lse_gpu, target_s):
+    """Times the fp64 oracle on query rows 0..n-1 of head 0 against all keys,
+    with n grown until the run takes about `target_s` seconds."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:   # pragma: no cover
+        threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    kh = k.values[:, :, :1]
+    vh = v.values[:, :, :1]
+
+    def run(n):
+        qh = q.values[:, :n, :1]
+        t0 = time.perf_counter()
+        if threadpool_limits:
+            with threadpool_limits(limits=cores, user_api="blas"):
+                out = oracle.attention_ref(qh, kh, vh, w.scale)
+        else:
+            out = oracle.attention_ref(qh, kh, vh, w.scale)
+        return time.perf_counter() - t0, out
+    n = 256
+    t, out = run(n)
+    if t < target_s:
+        n = int(min(w.Sq, max(256, n * target_s / max(t, 1e-3))) // 256 * 256) or 256
+        t, out = run(n)
+    flops = 4 * n * w.Skv * w.D
+    o_ref, lse_ref = out
+    og = o_gpu[:, :n, :1].cpu().numpy().astype(np.float64)
+    lg = lse_gpu[:, :1, :n].cpu().numpy().astype(np.float64)
+    err_o = float(np.abs(og - o_ref).max())
+    err_l = float(np.abs(lg - lse_ref).max())
+    log(f"[bench] cpu oracle: {n} rows x {w.Skv} keys, head 0: {t:.2f} s on {cores} cores "
+        f"({flops / t / 1e9:.1f} GFLOP/s fp64); GPU rows vs oracle: max|dO|={err_o:.2e} max|dLSE|={err_l:.2e}")
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"query rows 0..{n - 1} of head 0 against all {w.Skv} keys "
+                      f"({flops / 1e9:.1f} GFLOP, fp64 numpy, {t:.1f} s)",
+            "gpu_vs_oracle_on_sample": {"max_abs_dO": err_o, "max_abs_dLSE": err_l}}
+
+
+def traffic_entry(achieved_launch_ms):
+    """HBM bytes per launch of the headline kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except Exception:
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workloads", default="4,3,2,5",
+                    help="comma list; 4 (the headline) is always run")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target duration of the CPU oracle sample (0 disables)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import long_sequence_head_amd as L
+    import lsh_inputs as I
+    L.load()
+    torch.cuda.set_device(0)
+    wl = [int(x) for x in args.workloads.split(",") if x.strip()]
+    if 4 not in wl:
+        wl = [4] + wl
+
+    w4 = I.WORKLOADS[4]
+    head, keep = bench_dense(L, I, w4, args.steps, args.warmup)
+    secondary = {}
+    cpu = None
+    if args.cpu_seconds > 0:
+        q, k, v, o, lse = keep
+        cpu = cpu_baseline(I, w4, q, k, v, o, lse, args.cpu_seconds)
+    del keep
+    torch.cuda.empty_cache()
+    for wid in wl:
+        if wid == 4:
+            continue
+        w = I.WORKLOADS[wid]
+        if wid == 3:
+            secondary[w.name] = bench_chunked(L, I, w, args.steps, args.warmup)
+        elif wid == 2:
+            secondary[w.name] = bench_ring(L, I, w, args.steps, args.warmup)
+        elif wid == 5:
+            secondary[w.name] = bench_sparse(L, I, w, args.steps, args.warmup)
+        elif wid == 1:
+            r, _ = bench_dense(L, I, w, args.steps, args.warmup)
+            secondary[w.name] = r
+        torch.cuda.empty_cache()
+
+    ms = head["ms"]
+    achieved = head["flops"] / ms / 1e9     # one launch per step
+    line = {
+        "metric": METRIC,
+        "value": round(head["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded iid N(0,1) Q/K/V rounded to bf16 (lsh_inputs)",
+        "config": {"workload": w4.name, "B": w4.B, "S": w4.Sq, "H": w4.H, "D": w4.D,
+                   "causal": False, "out": "fp32 O [B,S,H,D] + fp32 LSE [B,H,S]"},
+        "pct_of_bf16_peak": round(100 * head["tflops"] / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_entry(ms),
+                     "kernel": "attn_fwd_bf16_kernel<8,false>",
+                     "algorithmic_flops_per_launch": head["flops"]},
+        "cpu_baseline": cpu,
+        "workloads": secondary,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
