@@ -258,6 +258,9 @@ def main():
                     help="comma list; 4 (the headline) is always run")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the CPU oracle sample (0 disables)")
+    ap.add_argument("--hbm-copy-probe", action="store_true",
+                    help="only run 10 plain 1 GiB device-to-device copies (calibrates HBM "
+                         "byte counters against a kernel of known traffic)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -266,6 +269,13 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.hbm_copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        ms, _ = timed(lambda: dst.copy_(src), 10, 2)
+        log(f"[bench] copy probe: 1 GiB read + 1 GiB write per call, {ms:.3f} ms, "
+            f"{2 * (1 << 30) / ms / 1e6:.0f} GB/s")
+        return
     import long_sequence_head_amd as L
     import lsh_inputs as I
     L.load()
