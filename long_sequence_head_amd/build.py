@@ -66,6 +66,12 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    # A kernel whose host-side instantiation was silently dropped leaves an
+    # undefined launch stub behind; refuse such a library.
+    nm = subprocess.run(["nm", "-u", "-C", tmp], capture_output=True, text=True)
+    missing = [l.strip() for l in nm.stdout.splitlines() if "lsh::" in l]
+    if missing:
+        raise RuntimeError("liblsh.so has undefined symbols of its own:\n" + "\n".join(missing))
     os.replace(tmp, out)
     return out
 

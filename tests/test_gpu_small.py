@@ -282,3 +282,23 @@ def test_blocksparse_diagonal_is_blockwise_dense(L):
         sl = slice(128 * i, 128 * (i + 1))
         o2, l2 = L.attn_fwd(qg[:, sl], kg[:, sl], vg[:, sl])
         assert t.equal(o1[:, sl], o2) and t.equal(l1[:, :, sl], l2), i
+
+
+@pytest.mark.parametrize("Skv", [1, 63, 64, 65, 128, 129, 191, 333, 1000, 4097])
+def test_eight_wave_kernel_ragged_keys(L, Skv):
+    """B*H*ceil(Sq/256) >= 512 launches the 8-wavefront kernel: sampled
+    query rows (incl. the ragged last query tile) against the oracle over
+    key counts that end mid-tile, at one tile, and below the prefetch depth."""
+    G.announce(f"8-wave ragged Skv={Skv}")
+    t = G.torch()
+    B, Sq, H = 1, 16400, 8
+    q, k, v = I.make_custom((B, Sq, H, 128), (B, Skv, H, 128), "bf16", seed=700 + Skv)
+    o, lse = G.poisoned_outputs(B, Sq, H)
+    L.attn_fwd(G.to_gpu(q, "bf16"), G.to_gpu(k, "bf16"), G.to_gpu(v, "bf16"), o=o, lse=lse)
+    t.cuda.synchronize()
+    assert not t.isnan(o).any() and not t.isnan(lse).any(), "unwritten output"
+    rows = I.sample_rows(Sq, 200, seed=Skv)
+    o_ref, lse_ref = oracle.attention_ref(q.values, k.values, v.values, 1 / math.sqrt(128), rows=rows)
+    ridx = t.from_numpy(rows).cuda()
+    G.check(f"8-wave Skv={Skv}", "bf16", o.index_select(1, ridx).cpu().numpy(),
+            lse.index_select(2, ridx).cpu().numpy(), o_ref, lse_ref)
