@@ -35,7 +35,6 @@
 //    kept in fp32.
 #include "lsh_internal.hpp"
 
-#include <cstdlib>
 #include <cstring>
 #include <type_traits>
 
@@ -843,20 +842,7 @@ __global__ void attn_empty_kernel(AttnParams p) {
   }
 }
 
-int env_int(const char* name, int dflt) {
-  const char* s = std::getenv(name);
-  if (!s || !*s) return dflt;
-  return std::atoi(s);
-}
-
 }  // namespace
-
-int dense_rows_per_block(DType dt, int64_t Sq) {
-  (void)Sq;
-  if (dt == DType::F32) return 4 * kQW;
-  static const int waves = env_int("LSH_DENSE_WAVES", 8);
-  return (waves == 4 ? 4 : 8) * kQW;
-}
 
 hipError_t launch_attn_dense(const AttnParams& p0, DType dt, hipStream_t s) {
   AttnParams p = p0;
@@ -866,11 +852,11 @@ hipError_t launch_attn_dense(const AttnParams& p0, DType dt, hipStream_t s) {
     hipLaunchKernelGGL((attn_fwd_f32_kernel<4, false>), dim3(p.n_items), dim3(256), 0, s, p);
     return hipGetLastError();
   }
-  int waves = dense_rows_per_block(dt, p.Sq) / kQW;
-  // Small grids: 4-wave workgroups spread better over 256 CUs. Per-query
-  // arithmetic is identical for either size.
+  // 8-wave ping-pong workgroups (256 query rows) once they give at least two
+  // workgroups per CU; smaller grids spread better as 4-wave workgroups (128
+  // rows). Per-query arithmetic is identical for either size.
   const int64_t items8 = (int64_t)p.B * p.H * ((p.Sq + 255) / 256);
-  if (waves == 8 && items8 < 512 && env_int("LSH_DENSE_WAVES", 0) == 0) waves = 4;
+  const int waves = items8 < 512 ? 4 : 8;
   const int bm = waves * kQW;
   p.n_qblk = (p.Sq + bm - 1) / bm;
   p.n_items = p.B * p.H * p.n_qblk;

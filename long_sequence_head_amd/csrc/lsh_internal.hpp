@@ -53,7 +53,4 @@ hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, int32_
 hipError_t launch_sparse_schedule(const uint8_t* mask, int32_t n_items, int32_t n_mkb,
                                   int32_t* counts, int32_t* order, hipStream_t s);
 
-// Query rows per workgroup of the dense kernel for a given query length.
-int dense_rows_per_block(DType dt, int64_t Sq);
-
 }  // namespace lsh
