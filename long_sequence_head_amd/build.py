@@ -20,6 +20,10 @@ LIBDIR = os.path.join(PKG, "lib")
 LIBNAME = "liblsh.so"
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["attn_fwd.hip", "aux_kernels.hip", "api.hip"]
+# Per-file code generation options. The attention kernels keep their MFMA
+# accumulators in VGPRs: the scores feed VALU work directly and the register
+# allocator otherwise shuttles them through AGPRs.
+FILE_FLAGS = {"attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = "gfx950"
 
 
@@ -56,7 +60,8 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     objs = []
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         futs = [ex.submit(_compile, os.path.join(CSRC, s),
-                          os.path.join(BUILD_DIR, s.replace(".hip", ".o")), extra_flags, verbose)
+                          os.path.join(BUILD_DIR, s.replace(".hip", ".o")),
+                          FILE_FLAGS.get(s, []) + list(extra_flags), verbose)
                 for s in SOURCES]
         for f in futs:
             objs.append(f.result())

@@ -10,13 +10,13 @@
 // for Visual Generative Models with Dual-Balanced Sequence Parallelism",
 // Abstract).
 //
-// Design (one wavefront = 32 query rows; a workgroup = WAVES wavefronts
-// sharing each key tile through LDS):
-//  * Q of the wavefront's 32 rows stays in VGPRs for the whole key loop.
-//  * Key tiles of 64 keys: K and V are staged HBM -> VGPR -> LDS, double
-//    buffered, one barrier per tile. K rows are XOR-swizzled by 16-byte
-//    chunk so the QK^T operand reads are bank-conflict free; V rows use a
-//    different swizzle matched to the transposing reads below.
+// Design, common to the bf16 kernels (a wavefront owns 32 query rows; the
+// wavefronts of a workgroup share each key tile through LDS):
+//  * Q of the wavefront's 32 rows stays in registers for the whole key loop.
+//  * Key tiles of 64 keys go straight from HBM into LDS slots with
+//    buffer_load ... lds. K rows are XOR-swizzled by 16-byte chunk so the
+//    QK^T operand reads are bank-conflict free; V rows use a different
+//    swizzle matched to the transposing reads below.
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: the accumulator puts one
 //    query per lane (lane l and l+32 share query l%32 and split the keys),
 //    so the row max and row sum need one cross-half swap only
@@ -29,10 +29,14 @@
 //    max only moves when a tile's max exceeds it by more than 2^8 in
 //    probability, so P stays <= 256 and the O rescale is skipped on almost
 //    every tile. Each query's arithmetic depends only on its own scores,
-//    so results do not depend on the workgroup size, the grid order, the
-//    number of heads or the strides.
-//  * fp32 inputs use v_mfma_f32_32x32x2_f32 with the same structure and P
-//    kept in fp32.
+//    in an order fixed per query, so results do not depend on the kernel
+//    chosen, the workgroup size, the grid order, the number of heads or the
+//    strides.
+// Two schedules implement it: a ping-pong kernel (two wavefronts per SIMD
+// alternating matrix and softmax phases) for large grids, and a
+// one-wavefront-per-SIMD software-pipelined kernel for small grids and the
+// block-sparse case. fp32 inputs use v_mfma_f32_32x32x2_f32 with the same
+// structure and P kept in fp32.
 #include "lsh_internal.hpp"
 
 #include <cstring>
@@ -138,219 +142,6 @@ __device__ __forceinline__ int tile_key0(int t, const unsigned short* kept) {
     return (int)kept[t >> 1] * kMaskBlock + (t & 1) * kBN;
   } else {
     return t * kBN;
-  }
-}
-
-// ----------------------------------------------------------------- bf16 path
-
-template <int WAVES, bool SPARSE>
-__global__ __launch_bounds__(WAVES * 64) void attn_fwd_bf16_kernel(AttnParams p) {
-  constexpr int NT = WAVES * 64;
-  constexpr int BM = WAVES * kQW;
-  constexpr int CPT = kBN * (kD / 8) / NT;  // 16-byte chunks per thread per tensor
-  static_assert(CPT >= 1 && CPT * NT == kBN * (kD / 8), "tile/threads mismatch");
-  static_assert(!SPARSE || BM == kMaskBlock, "sparse kernel works on one mask row");
-
-  __shared__ __attribute__((aligned(16))) __bf16 lds_k[2][kBN * kD];
-  __shared__ __attribute__((aligned(16))) __bf16 lds_v[2][kBN * kD];
-  extern __shared__ unsigned short kept_dyn[];
-  __shared__ int wave_cnt[WAVES];
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int l32 = lane & 31, hh = lane >> 5;
-
-  int item;
-  if constexpr (SPARSE) {
-    item = p.order ? p.order[blockIdx.x] : (int)blockIdx.x;
-  } else {
-    item = xcd_remap(blockIdx.x, gridDim.x);
-  }
-  const Item it = decode_item(item, p.n_qblk, p.H);
-  const int q0 = it.qblk * BM;
-  const int qi = q0 + wave * kQW + l32;
-  const bool q_ok = qi < p.Sq;
-
-  const __bf16* qp = static_cast<const __bf16*>(p.q) + it.b * p.q_sb + it.h * p.q_sh;
-  const __bf16* kp = static_cast<const __bf16*>(p.k) + it.b * p.k_sb + it.h * p.k_sh;
-  const __bf16* vp = static_cast<const __bf16*>(p.v) + it.b * p.v_sb + it.h * p.v_sh;
-
-  int n_tiles;
-  const unsigned short* kept = kept_dyn;
-  if constexpr (SPARSE) {
-    const uint8_t* mrow = p.mask + (((int64_t)it.b * p.H + it.h) * p.n_mqb + it.qblk) * p.n_mkb;
-    const int n_kept = build_kept_list<NT>(mrow, p.n_mkb, kept_dyn, wave_cnt);
-    n_tiles = 2 * n_kept;
-  } else {
-    n_tiles = (p.Skv + kBN - 1) / kBN;
-  }
-
-  // Q fragments: lane holds Q[qi][16 s + 8 hh .. +7], s = 0..7.
-  bf16x8 qf[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    if (q_ok) {
-      qf[s] = *reinterpret_cast<const bf16x8*>(qp + (int64_t)qi * p.q_ss + 16 * s + 8 * hh);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qf[s][i] = (__bf16)0.0f;
-    }
-  }
-
-  f32x16 acc[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
-  float m_run = kNegInf;  // running max of raw scores (both halves agree)
-  float l_run = 0.0f;     // this half's partial sum of exp2(s*c - m*c)
-  const float c = p.scale_log2;
-
-  u32x4 kst[CPT], vst[CPT];
-  auto gload = [&](int t) {
-    const int key0 = tile_key0<SPARSE>(t, kept);
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int cid = tid + i * NT;
-      const int row = cid >> 4, ch = cid & 15;
-      const int key = key0 + row;
-      if (key < p.Skv) {
-        kst[i] = *reinterpret_cast<const u32x4*>(kp + (int64_t)key * p.k_ss + ch * 8);
-        vst[i] = *reinterpret_cast<const u32x4*>(vp + (int64_t)key * p.v_ss + ch * 8);
-      } else {
-        kst[i] = u32x4{0u, 0u, 0u, 0u};
-        vst[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int cid = tid + i * NT;
-      const int row = cid >> 4, ch = cid & 15;
-      *reinterpret_cast<u32x4*>(&lds_k[buf][row * kD + swz_k(row, ch) * 8]) = kst[i];
-      *reinterpret_cast<u32x4*>(&lds_v[buf][row * kD + swz_v(row, ch) * 8]) = vst[i];
-    }
-  };
-
-  if (n_tiles > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) gload(t + 1);
-
-    // ---- S^T = K Q^T for the tile's 2 key blocks of 32
-    f32x16 st[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[kb][r] = 0.0f;
-      const int row = kb * 32 + l32;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(&lds_k[buf][row * kD + swz_k(row, 2 * s + hh) * 8]);
-        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], st[kb], 0, 0, 0);
-      }
-    }
-
-    // ---- mask keys past the end (last, partial tile only)
-    const int key0 = tile_key0<SPARSE>(t, kept);
-    if (key0 + kBN > p.Skv) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key >= p.Skv) st[kb][r] = kNegInf;
-        }
-    }
-
-    // ---- row max over this lane's 32 keys, then across the two halves
-    float mx = st[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
-    mx = pair_max(mx);
-
-    // ---- lazy rescale: move the running max only on a large increase
-    const bool need = (mx - m_run) * c > kRescaleLog2;
-    if (wave_any(need)) {
-      const float m_new = need ? mx : m_run;
-      const float alpha = need ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.0f;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-    }
-    const float mc = (m_run == kNegInf) ? 0.0f : m_run * c;
-
-    // ---- P = exp2(s c - m c), partial row sum, bf16 B operands
-    bf16x8 pf[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][r], c, -mc));
-        l_run += e;
-        pf[kb][r >> 3][r & 7] = (__bf16)e;
-      }
-
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        // transposing reads: lane (16 g + 4 e + a) points at key
-        // kb*32 + jj*16 + 8 part + 4 (g/2) + e, columns 32 db + 16 (g%2) + 4 a
-        const int g = lane >> 4, e = (lane >> 2) & 3, a = lane & 3;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          s16x4 w[2];
-#pragma unroll
-          for (int part = 0; part < 2; ++part) {
-            const int row = kb * 32 + jj * 16 + 8 * part + 4 * (g >> 1) + e;
-            const int col = db * 32 + 16 * (g & 1) + 4 * a;
-            const int off = row * kD + swz_v(row, col >> 3) * 8 + (col & 7);
-            w[part] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (LDS_AS s16x4*)((LDS_AS __bf16*)(&lds_v[buf][0]) + off));
-          }
-          // whole-vector assembly: slots 0-3 from the first read, 4-7 from the second
-          const s16x8 w8 = __builtin_shufflevector(w[0], w[1], 0, 1, 2, 3, 4, 5, 6, 7);
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, w8);
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][jj], acc[db], 0, 0, 0);
-        }
-      }
-
-    if (t + 1 < n_tiles) lstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue: combine halves, normalise, write O and LSE
-  const float l_tot = pair_sum(l_run);
-  if (!q_ok) return;
-  float* op = p.o + it.b * p.o_sb + it.h * p.o_sh + (int64_t)qi * p.o_ss;
-  const bool empty = !(l_tot > 0.0f);
-  const float inv_l = empty ? 0.0f : 1.0f / l_tot;
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = db * 32 + 8 * g4 + 4 * hh;
-      f32x4 o4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o4[i] = acc[db][4 * g4 + i] * inv_l;
-      *reinterpret_cast<f32x4*>(op + d) = o4;
-    }
-  if (hh == 0) {
-    const float lse = empty ? kNegInf : m_run * p.scale + __logf(l_tot);
-    p.lse[it.b * p.lse_sb + it.h * p.lse_sh + qi] = lse;
   }
 }
 
@@ -674,6 +465,367 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_bf16_pp_kernel(AttnParams
   }
 }
 
+// ------------------------------- bf16 dense, one wavefront per SIMD, pipelined
+//
+// Four wavefronts of 32 query rows each, one per SIMD. Each wavefront runs a
+// software pipeline over the key tiles, so that its own instruction stream
+// keeps the matrix core and the VALU busy together:
+//   phase 1 of step t: S(t+1) = K(t+1) Q^T (16 MFMA), interleaved with the
+//       exp2 of the already-scaled S(t) into x(t) (fp32) and P(t) (bf16);
+//   phase 2 of step t: O^T += V(t)^T P(t)^T (16 MFMA), interleaved with the
+//       row sum of x(t), the row max of S(t+1), the lazy-rescale decision and
+//       the scaling s c - m c of S(t+1).
+// Every query's arithmetic (product order, exp2 arguments, summation order,
+// rescale points, bf16 rounding of P) is the one of the other bf16 kernels,
+// so all of them give the same bits.
+//
+// K/V tiles go HBM -> LDS directly (buffer_load ... lds) into two slots per
+// tensor. Each slot is its own LDS variable and every access names its slot
+// at compile time (the step loop is unrolled by two), so the compiler can
+// tell the LDS reads of one slot from the loads in flight into the other and
+// does not make the reads wait for them. A step has two barriers: one after
+// phase 1 (all wavefronts are done with K(t+1)), one after phase 2 (done
+// with V(t)). Step t issues V(t+1) at its start, into the slot V(t-1) left,
+// and K(t+3) after its middle barrier, into the slot K(t+1) left; each load
+// has about one and a half steps to land, and a wavefront waits only for
+// the loads the next phase reads.
+
+constexpr int kSpWaves = 4;
+constexpr int kSpBM = kSpWaves * kQW;   // 128 query rows per workgroup
+
+template <bool SPARSE>
+__global__ __launch_bounds__(kSpWaves * 64, 1) void attn_fwd_bf16_sp_kernel(AttnParams p) {
+  constexpr int LPW = (kTileBytes / 1024) / kSpWaves;   // 1-KiB loads per wavefront per tensor
+  static_assert(LPW * kSpWaves * 1024 == kTileBytes, "tile/threads mismatch");
+  static_assert(!SPARSE || kSpBM == kMaskBlock, "a sparse workgroup covers one mask row");
+
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_v0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_v1[kTileBytes];
+  extern __shared__ unsigned short kept_dyn[];   // sparse: kept key blocks of the mask row
+  __shared__ int wave_cnt[kSpWaves];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  // Dense: workgroups walk the items XCD by XCD. Sparse: in the given order
+  // (most kept blocks first).
+  int item;
+  if constexpr (SPARSE) {
+    item = p.order ? p.order[blockIdx.x] : (int)blockIdx.x;
+  } else {
+    item = xcd_remap(blockIdx.x, gridDim.x);
+  }
+  const Item it = decode_item(item, p.n_qblk, p.H);
+  const int qi = it.qblk * kSpBM + wave * kQW + l32;
+  const bool q_ok = qi < p.Sq;
+  const __bf16* qp = static_cast<const __bf16*>(p.q) + it.b * p.q_sb + it.h * p.q_sh;
+  const __bf16* kp = static_cast<const __bf16*>(p.k) + it.b * p.k_sb + it.h * p.k_sh;
+  const __bf16* vp = static_cast<const __bf16*>(p.v) + it.b * p.v_sb + it.h * p.v_sh;
+
+  // Key tiles: dense, 64-key tiles in order; sparse, the two 64-key halves
+  // of every kept 128-key block in ascending order, without a half that lies
+  // wholly past the last key. Either way only the last tile can be ragged.
+  int n_tiles;
+  if constexpr (SPARSE) {
+    const uint8_t* mrow = p.mask + (((int64_t)it.b * p.H + it.h) * p.n_mqb + it.qblk) * p.n_mkb;
+    const int n_kept = build_kept_list<kSpWaves * 64>(mrow, p.n_mkb, kept_dyn, wave_cnt);
+    n_tiles = 2 * n_kept;
+    if (n_kept > 0 && (int)kept_dyn[n_kept - 1] * kMaskBlock + kBN >= p.Skv) n_tiles -= 1;
+  } else {
+    n_tiles = (p.Skv + kBN - 1) / kBN;
+  }
+  auto key0_of = [&](int t) __device__ -> int { return tile_key0<SPARSE>(t, kept_dyn); };
+
+  // Q fragments (B operand of S^T = K Q^T): lane holds Q[qi][16 s + 8 hh .. +7].
+  bf16x8 qf[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    qf[s] = q_ok ? *reinterpret_cast<const bf16x8*>(qp + (int64_t)qi * p.q_ss + 16 * s + 8 * hh)
+                 : bf16x8{};
+
+  // ---- tile loads: every wavefront issues LPW 1-KiB loads per tensor tile.
+  // Load j of this wavefront fills tile rows 4 (wave LPW + j) .. +3; lane l
+  // fills LDS chunk l%16 of its row, which holds the row's global chunk
+  // (l%16) ^ swizzle(row). A buffer resource over the head's rows makes
+  // loads past the last key return zeros.
+  const uint32_t k_rb = (uint32_t)(p.k_ss * 2), v_rb = (uint32_t)(p.v_ss * 2);
+  const int k_rec = (int)((uint32_t)(p.Skv - 1) * k_rb + kD * 2);
+  const int v_rec = (int)((uint32_t)(p.Skv - 1) * v_rb + kD * 2);
+  uint32_t koff[LPW], voff[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int r = 4 * (wave * LPW + j) + (lane >> 4);
+    const int pos = lane & 15;
+    koff[j] = (uint32_t)r * k_rb + ((uint32_t)swz_k(r, pos) << 4);
+    voff[j] = (uint32_t)r * v_rb + ((uint32_t)swz_v(r, pos) << 4);
+  }
+  auto kslot = [&](int slot) __device__ -> unsigned char* { return slot ? lds_k1 : lds_k0; };
+  auto vslot = [&](int slot) __device__ -> unsigned char* { return slot ? lds_v1 : lds_v0; };
+  auto issue_k = [&](int t) __device__ {
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)kp, (short)0, k_rec, 0x00020000);
+    const uint32_t base = (uint32_t)key0_of(t) * k_rb;
+    unsigned char* dst = kslot(t & 1) + wave * LPW * 1024;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(dst + j * 1024), 16,
+                                               (int)(koff[j] + base), 0, 0, 0);
+  };
+  auto issue_v = [&](int t) __device__ {
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)vp, (short)0, v_rec, 0x00020000);
+    const uint32_t base = (uint32_t)key0_of(t) * v_rb;
+    unsigned char* dst = vslot(t & 1) + wave * LPW * 1024;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(dst + j * 1024), 16,
+                                               (int)(voff[j] + base), 0, 0, 0);
+  };
+
+  // ---- LDS fragment offsets inside a tile (per lane, loop-invariant). K
+  // fragment i = 2 s + kb reads row kb*32 + l32, head_dim 16 s + 8 hh .. +7.
+  // V^T fragment i = (kb*2 + jj)*4 + db comes from two transposing reads:
+  // lane (16 g + 4 e + a) points at key kb*32 + jj*16 + 8 part + 4 (g/2) + e,
+  // columns 32 db + 16 (g%2) + 4 a, and receives 4 keys of column 32 db + l%32.
+  uint32_t kofs[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) kofs[s] = (uint32_t)(l32 * 256 + (swz_k(l32, 2 * s + hh) << 4));
+  const int tg = lane >> 4, te = (lane >> 2) & 3, ta = lane & 3;
+  uint32_t vofs[2][4];
+#pragma unroll
+  for (int part = 0; part < 2; ++part)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int row = 8 * part + 4 * (tg >> 1) + te;
+      const int col = db * 32 + 16 * (tg & 1) + 4 * ta;
+      vofs[part][db] = (uint32_t)(row * 256 + (swz_v(row, col >> 3) << 4) + (col & 7) * 2);
+    }
+  auto kread = [&](int slot, int i) __device__ -> bf16x8 {
+    const LDS_AS unsigned char* b = (LDS_AS const unsigned char*)kslot(slot);
+    return *(LDS_AS const bf16x8*)(b + kofs[i >> 1] + (i & 1) * 8192);
+  };
+  auto vread = [&](int slot, int i) __device__ -> bf16x8 {
+    const int db = i & 3, jj = (i >> 2) & 1, kb = i >> 3;
+    const LDS_AS unsigned char* b = (LDS_AS const unsigned char*)vslot(slot) + (kb * 32 + jj * 16) * 256;
+    const s16x4 w0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(b + vofs[0][db]));
+    const s16x4 w1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(b + vofs[1][db]));
+    const s16x8 w8 = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, w8);
+  };
+
+  // ---- softmax state
+  const float c = p.scale_log2;
+  f32x16 acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
+  float m_run = kNegInf;   // running max of raw scores (both halves agree)
+  float mc = 0.0f;         // m_run * c, or 0 while m_run = -inf
+  float l_run = 0.0f;      // this half's partial sum of exp2(s c - m c)
+  f32x16 sa[2], sb[2];     // S of two consecutive tiles: st[kb][r]
+  bf16x8 pf[2][2];         // P(t): pf[kb][jj]
+
+  // Row max of the raw scores st -> lazy-rescale decision -> st becomes
+  // s c - m c. Split into 16 slices that phase 2 spreads over its 16 MFMAs:
+  // slices 0-7 take the max of scores 4k .. 4k+3, slice 8 decides, slices
+  // 9-15 scale five scores each.
+  float part_max = kNegInf, alpha = 1.0f;
+  bool any_need = false;
+  auto softmax_slice = [&](f32x16 (&st)[2], int k) __device__ {
+    if (k < 8) {
+#pragma unroll
+      for (int e = 4 * k; e < 4 * k + 4; ++e) part_max = fmaxf(part_max, st[e >> 4][e & 15]);
+    } else if (k == 8) {
+      const float mx = pair_max(part_max);
+      part_max = kNegInf;
+      const bool need = (mx - m_run) * c > kRescaleLog2;
+      const float m_new = need ? mx : m_run;
+      alpha = need ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.0f;
+      any_need = wave_any(need);
+      m_run = m_new;
+      mc = (m_run == kNegInf) ? 0.0f : m_run * c;
+    } else {
+      const int e0 = 5 * (k - 9), e1 = e0 + 5 < 32 ? e0 + 5 : 32;
+#pragma unroll
+      for (int e = e0; e < e1; ++e) {
+        float y = __builtin_fmaf(st[e >> 4][e & 15], c, -mc);
+        asm volatile("" : "+v"(y));   // computed here, not sunk into the next step
+        st[e >> 4][e & 15] = y;
+      }
+    }
+  };
+  auto mask_tile = [&](f32x16 (&st)[2], int key0) __device__ {
+    if (key0 + kBN > p.Skv) {
+      const int lim = p.Skv - key0 - 4 * hh;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + (r & 3);
+        if (off >= lim) st[0][r] = kNegInf;
+        if (off + 32 >= lim) st[1][r] = kNegInf;
+      }
+    }
+  };
+
+  // phase 1 of step t: S(t+1) -> sn (if DO_QK), interleaved with
+  // x(t) = exp2(sc) kept in sc and P(t) = bf16(x(t)) in pf
+  auto phase1 = [&](const bool DO_QK, int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) __device__ {
+    const int ks = (t + 1) & 1;
+    bf16x8 kf[16];
+    if (DO_QK) {
+      kf[0] = kread(ks, 0);
+      kf[1] = kread(ks, 1);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (DO_QK) {
+        if (i + 2 < 16) kf[i + 2] = kread(ks, i + 2);
+        if (i < 2)
+          sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i >> 1], f32x16{}, 0, 0, 0);
+        else
+          sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i >> 1], sn[i & 1], 0, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int e = 2 * i + q, kb = e >> 4, r = e & 15;
+        const float x = __builtin_amdgcn_exp2f(sc[kb][r]);
+        asm volatile("" ::"v"(x));   // computed here, next to this MFMA
+        sc[kb][r] = x;
+        pf[kb][r >> 3][r & 7] = (__bf16)x;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // phase 2 of step t: O^T += V(t)^T P(t)^T, interleaved with l += x(t) and
+  // (if HAS_NEXT) the softmax slices of S(t+1)
+  auto phase2 = [&](const bool HAS_NEXT, const bool MAYBE_RAGGED, int t, f32x16 (&sc)[2],
+                    f32x16 (&sn)[2]) __device__ {
+    if (HAS_NEXT && MAYBE_RAGGED) mask_tile(sn, key0_of(t + 1));
+    const int vs = t & 1;
+    bf16x8 vf[16];
+    vf[0] = vread(vs, 0);
+    vf[1] = vread(vs, 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i + 2 < 16) vf[i + 2] = vread(vs, i + 2);
+      const int db = i & 3, jj = (i >> 2) & 1, kb = i >> 3;
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[kb][jj], acc[db], 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int e = 2 * i + q;
+        float l = l_run + sc[e >> 4][e & 15];
+        asm volatile("" : "+v"(l));   // summed here, in key order
+        l_run = l;
+      }
+      if (HAS_NEXT) softmax_slice(sn, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (HAS_NEXT) {
+      l_run *= alpha;
+      if (any_need) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) acc[db] *= alpha;
+      }
+    }
+  };
+
+  // waits until at most n (0, LPW or 2 LPW) of this wavefront's loads are
+  // still in flight
+  auto wait_le = [&](int n) __device__ {
+    if (n == 0) wait_vmcnt<0>();
+    else if (n == LPW) wait_vmcnt<LPW>();
+    else wait_vmcnt<2 * LPW>();
+  };
+
+  // A sparse row without kept blocks attends to no key: it skips straight
+  // to the epilogue, which writes O = 0 and LSE = -inf.
+  if (n_tiles > 0) {
+    // ---- prologue: K0, K1 and V0 in flight; S(0), its max, the rescale
+    // decision and its scaling once K0 landed; then K1 must have landed and
+    // K2 goes into K0's slot.
+    issue_k(0);
+    if (n_tiles > 1) issue_k(1);
+    issue_v(0);
+    wait_le(n_tiles > 1 ? 2 * LPW : LPW);
+    barrier_no_fence();
+    {
+      sa[0] = f32x16{};
+      sa[1] = f32x16{};
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        sa[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(0, i), qf[i >> 1], sa[i & 1], 0, 0, 0);
+      mask_tile(sa, key0_of(0));
+#pragma unroll
+      for (int k = 0; k < 16; ++k) softmax_slice(sa, k);
+      l_run *= alpha;   // l_run = 0: the product stays 0
+    }
+    wait_le(LPW);   // K1 (V0 may stay in flight)
+    barrier_no_fence();
+    if (n_tiles > 2) issue_k(2);
+
+    // one step: tile t's scaled scores in sc, S(t+1) into sn (if HAS_NEXT,
+    // i.e. t + 1 < n_tiles)
+    auto step = [&](const bool HAS_NEXT, const bool MAYBE_RAGGED, int t, f32x16 (&sc)[2],
+                    f32x16 (&sn)[2]) __device__ {
+      if (HAS_NEXT) issue_v(t + 1);
+      phase1(HAS_NEXT, t, sc, sn);
+      // V(t) next; in flight after it: K(t+2), V(t+1)
+      wait_le((t + 2 < n_tiles ? LPW : 0) + (HAS_NEXT ? LPW : 0));
+      barrier_no_fence();
+      if (t + 3 < n_tiles) issue_k(t + 3);
+      phase2(HAS_NEXT, MAYBE_RAGGED, t, sc, sn);
+      if (t + 2 < n_tiles) {
+        // K(t+2) next; in flight after it: V(t+1), K(t+3)
+        wait_le((HAS_NEXT ? LPW : 0) + (t + 3 < n_tiles ? LPW : 0));
+        barrier_no_fence();
+      }
+    };
+
+    // t is even at the top of the loop, so every slot index above is a
+    // compile-time constant. Tiles before the last one are never ragged: the
+    // loop runs steps whose next tile is at most n_tiles - 2.
+    int t = 0;
+    for (; t + 3 < n_tiles; t += 2) {
+      step(true, false, t, sa, sb);
+      step(true, false, t + 1, sb, sa);
+    }
+    const int rest = n_tiles - t;   // 1, 2 or 3
+    if (rest == 3) {
+      step(true, false, t, sa, sb);
+      step(true, true, t + 1, sb, sa);
+      step(false, false, t + 2, sa, sa);
+    } else if (rest == 2) {
+      step(true, true, t, sa, sb);
+      step(false, false, t + 1, sb, sb);
+    } else {
+      step(false, false, t, sa, sa);
+    }
+  }   // n_tiles > 0
+
+  // ---- epilogue: combine halves, normalise, write O and LSE
+  const float l_tot = pair_sum(l_run);
+  if (!q_ok) return;
+  float* op = p.o + it.b * p.o_sb + it.h * p.o_sh + (int64_t)qi * p.o_ss;
+  const bool empty = !(l_tot > 0.0f);
+  const float inv_l = empty ? 0.0f : 1.0f / l_tot;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = db * 32 + 8 * g4 + 4 * hh;
+      f32x4 o4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o4[i] = acc[db][4 * g4 + i] * inv_l;
+      *reinterpret_cast<f32x4*>(op + d) = o4;
+    }
+  if (hh == 0) {
+    const float lse = empty ? kNegInf : m_run * p.scale + __logf(l_tot);
+    p.lse[it.b * p.lse_sb + it.h * p.lse_sh + qi] = lse;
+  }
+}
+
 // ------------------------------------------------------------------ f32 path
 
 // LDS row stride (floats) of the fp32 tiles: padded against bank conflicts.
@@ -852,18 +1004,19 @@ hipError_t launch_attn_dense(const AttnParams& p0, DType dt, hipStream_t s) {
     hipLaunchKernelGGL((attn_fwd_f32_kernel<4, false>), dim3(p.n_items), dim3(256), 0, s, p);
     return hipGetLastError();
   }
-  // 8-wave ping-pong workgroups (256 query rows) once they give at least two
-  // workgroups per CU; smaller grids spread better as 4-wave workgroups (128
-  // rows). Per-query arithmetic is identical for either size.
-  const int64_t items8 = (int64_t)p.B * p.H * ((p.Sq + 255) / 256);
-  const int waves = items8 < 512 ? 4 : 8;
-  const int bm = waves * kQW;
-  p.n_qblk = (p.Sq + bm - 1) / bm;
-  p.n_items = p.B * p.H * p.n_qblk;
-  if (waves == 8)
+  // Grids of at least two 256-row workgroups per CU run the ping-pong
+  // kernel; smaller ones the one-wavefront-per-SIMD kernel, which keeps every
+  // SIMD busy with a single 128-row workgroup per CU. Both give the same bits.
+  const int64_t items_pp = (int64_t)p.B * p.H * ((p.Sq + 255) / 256);
+  if (items_pp >= 512) {
+    p.n_qblk = (p.Sq + 255) / 256;
+    p.n_items = p.B * p.H * p.n_qblk;
     hipLaunchKernelGGL((attn_fwd_bf16_pp_kernel<8>), dim3(p.n_items), dim3(512), 0, s, p);
-  else
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<4, false>), dim3(p.n_items), dim3(256), 0, s, p);
+  } else {
+    p.n_qblk = (p.Sq + kSpBM - 1) / kSpBM;
+    p.n_items = p.B * p.H * p.n_qblk;
+    hipLaunchKernelGGL(attn_fwd_bf16_sp_kernel<false>, dim3(p.n_items), dim3(kSpWaves * 64), 0, s, p);
+  }
   return hipGetLastError();
 }
 
@@ -875,7 +1028,7 @@ hipError_t launch_attn_sparse(const AttnParams& p0, DType dt, hipStream_t s) {
   if (dt == DType::F32)
     hipLaunchKernelGGL((attn_fwd_f32_kernel<4, true>), dim3(p.n_items), dim3(256), dyn, s, p);
   else
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<4, true>), dim3(p.n_items), dim3(256), dyn, s, p);
+    hipLaunchKernelGGL(attn_fwd_bf16_sp_kernel<true>, dim3(p.n_items), dim3(kSpWaves * 64), dyn, s, p);
   return hipGetLastError();
 }
 
