@@ -61,6 +61,7 @@ __global__ __launch_bounds__(kPermThreads) void head_permute_kernel(
 // bottleneck). One (b, s, h) row of 128 floats per 32 lanes, float4 each;
 // consecutive rows are contiguous in O.
 constexpr int kMergeThreads = 256;
+constexpr int kMergeGroup = 8;
 
 __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(
     const float* __restrict__ o_parts, const float* __restrict__ lse_parts, int n, int B, int Sq,
@@ -83,13 +84,29 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float out_lse = kNegInf;
   if (M != kNegInf) {
+    // Partials in groups of kMergeGroup: all loads of a group are issued
+    // before any is used, so many bytes are in flight per lane; the sums
+    // still run over k = 0, 1, ... in order.
     float Z = 0.0f;
-    for (int k = 0; k < n; ++k) {
-      const float w = expf(lse_parts[k * lse_step + lse_off] - M);
-      const f32x4 ok = __builtin_nontemporal_load(
-          reinterpret_cast<const f32x4*>(o_parts + k * o_step + (int64_t)row * kD) + l);
-      acc += w * ok;
-      Z += w;
+    for (int k0 = 0; k0 < n; k0 += kMergeGroup) {
+      f32x4 ok[kMergeGroup];
+      float w[kMergeGroup];
+#pragma unroll
+      for (int j = 0; j < kMergeGroup; ++j) {
+        if (k0 + j < n) {
+          w[j] = lse_parts[(k0 + j) * lse_step + lse_off];
+          ok[j] = __builtin_nontemporal_load(
+              reinterpret_cast<const f32x4*>(o_parts + (k0 + j) * o_step + (int64_t)row * kD) + l);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kMergeGroup; ++j) {
+        if (k0 + j < n) {
+          const float wj = expf(w[j] - M);
+          acc += wj * ok[j];
+          Z += wj;
+        }
+      }
     }
     acc *= 1.0f / Z;
     out_lse = M + logf(Z);
@@ -121,26 +138,41 @@ __global__ __launch_bounds__(256) void sparse_count_kernel(const uint8_t* __rest
   if (lane == 0) counts[item] = cnt;
 }
 
-// order[rank(i)] = i with rank(i) = #{j : key_j > key_i},
-// key_j = (counts[j] << 32) | (n - 1 - j): descending count, ascending item
-// index among equal counts. Deterministic. 64 items per block, the 4
-// wavefronts split the j range.
-__global__ __launch_bounds__(256) void sparse_rank_kernel(const int* __restrict__ counts, int n,
-                                                          int* __restrict__ order) {
-  __shared__ int part[4][64];
+// order[rank(i)] = i with rank(i) = #{j : c_j > c_i} + #{j < i : c_j = c_i}
+// (c = counts): descending count, ascending item index among equal counts,
+// so the order is deterministic. A workgroup ranks 64 items; its 16
+// wavefronts split the j range, reading the counts from LDS in chunks
+// (every lane of a wavefront reads the same entry: a broadcast).
+constexpr int kRankWaves = 16;
+constexpr int kRankChunk = 4096;
+
+__global__ __launch_bounds__(kRankWaves * 64) void sparse_rank_kernel(const int* __restrict__ counts,
+                                                                     int n,
+                                                                     int* __restrict__ order) {
+  __shared__ int cbuf[kRankChunk];
+  __shared__ int part[kRankWaves][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i = blockIdx.x * 64 + lane;
-  const unsigned long long key_i =
-      i < n ? (((unsigned long long)(unsigned)counts[i]) << 32) | (unsigned)(n - 1 - i) : 0ull;
+  const int c_i = i < n ? counts[i] : 0;
   int r = 0;
-  for (int j = w; j < n; j += 4) {
-    const unsigned long long key_j =
-        (((unsigned long long)(unsigned)counts[j]) << 32) | (unsigned)(n - 1 - j);
-    r += key_j > key_i;
+  for (int base = 0; base < n; base += kRankChunk) {
+    const int m = n - base < kRankChunk ? n - base : kRankChunk;
+    __syncthreads();
+    for (int j = threadIdx.x; j < m; j += kRankWaves * 64) cbuf[j] = counts[base + j];
+    __syncthreads();
+    for (int jj = w; jj < m; jj += kRankWaves) {
+      const int c_j = cbuf[jj];
+      r += (c_j > c_i) | ((c_j == c_i) & (base + jj < i));
+    }
   }
   part[w][lane] = r;
   __syncthreads();
-  if (w == 0 && i < n) order[part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane]] = i;
+  if (w == 0 && i < n) {
+    int rank = 0;
+#pragma unroll
+    for (int k = 0; k < kRankWaves; ++k) rank += part[k][lane];
+    order[rank] = i;
+  }
 }
 
 }  // namespace
@@ -174,7 +206,7 @@ hipError_t launch_sparse_schedule(const uint8_t* mask, int32_t n_items, int32_t 
                      n_mkb, counts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(sparse_rank_kernel, dim3((n_items + 63) / 64), dim3(256), 0, s, counts,
+  hipLaunchKernelGGL(sparse_rank_kernel, dim3((n_items + 63) / 64), dim3(kRankWaves * 64), 0, s, counts,
                      n_items, order);
   return hipGetLastError();
 }

@@ -146,8 +146,9 @@ def test_run_to_run_bit_identical(L):
 
 
 def test_workgroup_size_does_not_change_bits(L):
-    """Head 0 alone launches 4-wave workgroups, all 8 heads launch 8-wave
-    ones; chunking {1, 7} vs unchunked compares the two bit for bit."""
+    """Head 0 alone (64 workgroups) runs the one-wavefront-per-SIMD kernel,
+    all 8 heads (512 workgroups of 256 rows) the 8-wavefront ping-pong
+    kernel; chunking {1, 7} vs unchunked compares the two bit for bit."""
     G.announce("workgroup-size invariance")
     t = G.torch()
     S, H = 16384, 8
@@ -233,6 +234,8 @@ def test_merge_all_empty(L):
 
 SPARSE_CASES = [  # (Sq, Skv, H)
     (128, 128, 1), (300, 257, 2), (640, 1000, 2), (1024, 1024, 3),
+    # last key block holding exactly 64 keys (its second half is empty) and 65
+    (256, 320, 2), (256, 321, 2),
 ]
 
 
