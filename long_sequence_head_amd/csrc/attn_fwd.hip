@@ -32,11 +32,11 @@
 //    in an order fixed per query, so results do not depend on the kernel
 //    chosen, the workgroup size, the grid order, the number of heads or the
 //    strides.
-// Two schedules implement it: a ping-pong kernel (two wavefronts per SIMD
-// alternating matrix and softmax phases) for large grids, and a
-// one-wavefront-per-SIMD software-pipelined kernel for small grids and the
-// block-sparse case. fp32 inputs use v_mfma_f32_32x32x2_f32 with the same
-// structure and P kept in fp32.
+// The bf16 kernel runs one wavefront per SIMD and software-pipelines each
+// wavefront's key loop (matrix work of one tile interleaved with the softmax
+// work of its neighbour); it serves dense and block-sparse attention. fp32
+// inputs use v_mfma_f32_32x32x2_f32 with the same structure and P kept in
+// fp32.
 #include "lsh_internal.hpp"
 
 #include <cstring>
@@ -52,6 +52,7 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -145,35 +146,9 @@ __device__ __forceinline__ int tile_key0(int t, const unsigned short* kept) {
   }
 }
 
-// ------------------------------------------- bf16 dense, ping-pong schedule
-//
-// The 8 wavefronts of a workgroup form two groups of four, one wavefront of
-// each group per SIMD. Every wavefront alternates two phases separated by
-// workgroup barriers:
-//   Q-phase(t): S(t) = K(t) Q^T                       (16 MFMA, no VALU work)
-//   P-phase(t): row max, lazy rescale and exp2 of S(t) -> P(t), interleaved
-//               with O^T += V(t-1)^T P(t-1)^T          (16 MFMA, ~130 VALU)
-// and group B runs one phase behind group A, so on each SIMD one wavefront
-// feeds the matrix core with QK^T while the other one's softmax keeps the
-// VALU busy next to its PV products.
-//
-// K/V tiles stream through a 3-slot LDS ring per tensor, filled with
-// buffer_load_dwordx4 ... lds (each lane's 16 bytes land at slot base + 16 *
-// lane; loads past the head's last key return zeros: the zero fill of a
-// ragged last tile). Intervals between barriers are numbered k = 0, 1, ...;
-// K(t) is issued in interval 2t-4 and V(t) in interval 2t-1, so every load
-// has two intervals to land; a wavefront waits only for loads issued two
-// or more intervals back (s_waitcnt vmcnt) before the barrier, and no fence
-// drains the prefetch. A slot is refilled only after the barrier that
-// follows its last reader.
+// ------------------------------------------------------- shared helpers
 
-constexpr int kStages = 3;
 constexpr int kTileBytes = kBN * kD * 2;   // one 64 x 128 bf16 tile
-
-// LDS byte addresses of one tile's K fragments (by d-step) and V^T fragment
-// reads (by half and d block).
-struct KAddr { uint32_t a[8]; };
-struct VAddr { uint32_t a[2][4]; };
 
 // s_waitcnt with vmcnt = N (6 bits: [3:0] and [15:14]); expcnt and lgkmcnt
 // left at their maximum.
@@ -189,283 +164,35 @@ __device__ __forceinline__ void barrier_no_fence() {
   asm volatile("" ::: "memory");
 }
 
-template <int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void attn_fwd_bf16_pp_kernel(AttnParams p) {
-  static_assert(WAVES == 8, "two groups of one wavefront per SIMD");
-  constexpr int BM = WAVES * kQW;
-  constexpr int LPW = (kTileBytes / 1024) / (WAVES / 2);   // 1-KiB loads per wavefront per tile
-  static_assert(LPW >= 1 && LPW * (WAVES / 2) * 1024 == kTileBytes, "tile/threads mismatch");
-
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_k[kStages][kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_v[kStages][kTileBytes];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hh = lane >> 5;
-  const bool grp_b = wave >= WAVES / 2;
-
-  const Item it = decode_item(xcd_remap(blockIdx.x, gridDim.x), p.n_qblk, p.H);
-  const int qi = it.qblk * BM + wave * kQW + l32;
-  const bool q_ok = qi < p.Sq;
-  const __bf16* qp = static_cast<const __bf16*>(p.q) + it.b * p.q_sb + it.h * p.q_sh;
-  const __bf16* kp = static_cast<const __bf16*>(p.k) + it.b * p.k_sb + it.h * p.k_sh;
-  const __bf16* vp = static_cast<const __bf16*>(p.v) + it.b * p.v_sb + it.h * p.v_sh;
-  const int n_tiles = (p.Skv + kBN - 1) / kBN;
-
-  // Q fragments (B operand of S^T = K Q^T): lane holds Q[qi][16 s + 8 hh .. +7].
-  bf16x8 qf[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s)
-    qf[s] = q_ok ? *reinterpret_cast<const bf16x8*>(qp + (int64_t)qi * p.q_ss + 16 * s + 8 * hh)
-                 : bf16x8{};
-
-  // Load streams: the wavefronts of group A stream K tiles into the K ring,
-  // those of group B stream V tiles into the V ring; each issues its share
-  // (LPW 1-KiB loads) at the start of its own Q-phase. A buffer resource
-  // over the head's rows makes loads past the last key return zeros.
-  const int wl = wave % (WAVES / 2);   // index inside the group
-  const uint32_t k_rb = (uint32_t)(p.k_ss * 2), v_rb = (uint32_t)(p.v_ss * 2);
-  const uint32_t my_rb = grp_b ? v_rb : k_rb;
-  const void* my_src = grp_b ? (const void*)vp : (const void*)kp;
-  const int my_rec = (int)((uint32_t)(p.Skv - 1) * my_rb + kD * 2);
-  // Load j of this wavefront fills tile rows 4 (wl LPW + j) .. +3; lane l
-  // fills LDS chunk l%16 of its row, which holds the row's global chunk
-  // (l%16) ^ swizzle(row).
-  uint32_t loff[LPW];
-#pragma unroll
-  for (int j = 0; j < LPW; ++j) {
-    const int r = 4 * (wl * LPW + j) + (lane >> 4);
-    const int pos = lane & 15;
-    const int chunk = grp_b ? swz_v(r, pos) : swz_k(r, pos);
-    loff[j] = (uint32_t)r * my_rb + ((uint32_t)chunk << 4);
-  }
-  unsigned char* my_ring = grp_b ? &lds_v[0][0] : &lds_k[0][0];
-  auto issue = [&](int t) __device__ {
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)my_src, (short)0, my_rec, 0x00020000);
-    const uint32_t base = (uint32_t)(t * kBN) * my_rb;
-    unsigned char* dst = my_ring + (t % kStages) * kTileBytes + wl * LPW * 1024;
-#pragma unroll
-    for (int j = 0; j < LPW; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(dst + j * 1024), 16,
-                                               (int)(loff[j] + base), 0, 0, 0);
-  };
-
-  const float c = p.scale_log2;
-  f32x16 acc[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
-  float m_run = kNegInf;  // running max of raw scores (both halves agree)
-  float l_run = 0.0f;     // this half's partial sum of exp2(s c - m c)
-
-  // Per-lane LDS byte offsets inside a tile, computed once. K fragment
-  // i = 2 s + kb reads row kb*32 + l32, head_dim 16 s + 8 hh .. +7; the row's
-  // swizzle depends on l32 only, so kb adds a plain 8 KiB.
-  uint32_t kofs[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) kofs[s] = (uint32_t)(l32 * 256 + (swz_k(l32, 2 * s + hh) << 4));
-  // V^T fragment i = (kb*2 + jj)*4 + db comes from two transposing reads:
-  // lane (16 g + 4 e + a) points at key kb*32 + jj*16 + 8 part + 4 (g/2) + e,
-  // columns 32 db + 16 (g%2) + 4 a, and receives 4 keys of column 32 db + l%32.
-  // The swizzle of row kb*32 + jj*16 + r depends on r only, so (kb, jj) add
-  // plain multiples of 4 KiB.
-  const int tg = lane >> 4, te = (lane >> 2) & 3, ta = lane & 3;
-  uint32_t vofs[2][4];
-#pragma unroll
-  for (int part = 0; part < 2; ++part)
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int row = 8 * part + 4 * (tg >> 1) + te;
-      const int col = db * 32 + 16 * (tg & 1) + 4 * ta;
-      vofs[part][db] = (uint32_t)(row * 256 + (swz_v(row, col >> 3) << 4) + (col & 7) * 2);
-    }
-  // LDS byte addresses of the two rings, hidden from constant folding so
-  // that per-phase addresses stay "register base + small immediate" instead
-  // of dozens of hoisted absolute addresses.
-  uint32_t lds_k_addr = (uint32_t)(uintptr_t)(LDS_AS unsigned char*)&lds_k[0][0];
-  uint32_t lds_v_addr = (uint32_t)(uintptr_t)(LDS_AS unsigned char*)&lds_v[0][0];
-  asm volatile("" : "+s"(lds_k_addr));
-  asm volatile("" : "+s"(lds_v_addr));
-  auto k_addr = [&](int t) __device__ -> KAddr {
-    KAddr r;
-    const uint32_t base = lds_k_addr + (uint32_t)(t % kStages) * kTileBytes;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      uint32_t o = kofs[s];
-      asm volatile("" : "+v"(o));   // recomputed per phase: nothing to hoist
-      r.a[s] = o + base;
-    }
-    return r;
-  };
-  auto v_addr = [&](int t) __device__ -> VAddr {
-    VAddr r;
-    const uint32_t base = lds_v_addr + (uint32_t)(t % kStages) * kTileBytes;
-#pragma unroll
-    for (int part = 0; part < 2; ++part)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        uint32_t o = vofs[part][db];
-        asm volatile("" : "+v"(o));
-        r.a[part][db] = o + base;
-      }
-    return r;
-  };
-  auto kread = [&](const KAddr& ka, int i) __device__ -> bf16x8 {
-    return *(LDS_AS const bf16x8*)(uintptr_t)(ka.a[i >> 1] + (i & 1) * 8192);
-  };
-  auto vread = [&](const VAddr& va, int i) __device__ -> bf16x8 {
-    const int db = i & 3, jj = (i >> 2) & 1, kb = i >> 3;
-    const uint32_t off = (kb * 32 + jj * 16) * 256;
-    const s16x4 w0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(uintptr_t)(va.a[0][db] + off));
-    const s16x4 w1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(uintptr_t)(va.a[1][db] + off));
-    const s16x8 w8 = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8, w8);
-  };
-
-  f32x16 st[2];                   // S(t) of the current Q/P pair
-  bf16x8 pf0[2][2], pf1[2][2];    // P(t) for even / odd t
-
-  auto q_phase = [&](int t) __device__ {
-    const KAddr kt = k_addr(t);
-    bf16x8 kf[16];
-    kf[0] = kread(kt, 0);
-    kf[1] = kread(kt, 1);
-    st[0] = f32x16{};
-    st[1] = f32x16{};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i + 2 < 16) kf[i + 2] = kread(kt, i + 2);
-      st[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i >> 1], st[i & 1], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);   // keep reads two MFMAs ahead, no further
-    }
-  };
-
-  // P-phase of tile t: P(t) into pc; O^T += V(t-1)^T P(t-1)^T from pp.
-  auto p_phase = [&](const bool WITH_PV, int t, bf16x8 (&pc)[2][2], bf16x8 (&pp)[2][2]) {
-    const VAddr vt = v_addr(t + kStages - 1);
-    bf16x8 vf[16];
-    if (WITH_PV) {
-      vf[0] = vread(vt, 0);
-      vf[1] = vread(vt, 1);
-    }
-    const int key0 = t * kBN;
-    if (key0 + kBN > p.Skv) {   // ragged last tile: keys past Skv do not exist
-#pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const int r = e & 15;
-        const int key = key0 + (e >> 4) * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (key >= p.Skv) st[e >> 4][r] = kNegInf;
-      }
-    }
-    float mx = st[0][0];
-#pragma unroll
-    for (int e = 1; e < 32; ++e) mx = fmaxf(mx, st[e >> 4][e & 15]);
-    mx = pair_max(mx);
-    // lazy rescale: move the running max only on an increase above 2^8
-    const bool need = (mx - m_run) * c > kRescaleLog2;
-    const float m_new = need ? mx : m_run;
-    const float alpha = need ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.0f;
-    const bool any_need = wave_any(need);
-    l_run *= alpha;
-    m_run = m_new;
-    const float mc = (m_run == kNegInf) ? 0.0f : m_run * c;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (WITH_PV) {
-        if (i + 2 < 16) vf[i + 2] = vread(vt, i + 2);
-        const int db = i & 3, jj = (i >> 2) & 1, kb = i >> 3;
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pp[kb][jj], acc[db], 0, 0, 0);
-      }
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int e = 2 * i + q, kb = e >> 4, r = e & 15;
-        const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][r], c, -mc));
-        l_run += x;
-        pc[kb][r >> 3][r & 7] = (__bf16)x;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (any_need) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db) acc[db] *= alpha;
-    }
-  };
-
-  // ---- prologue: group A loads K0 and K1, group B loads V0; all land
-  // before interval 0.
-  if (!grp_b) {
-    issue(0);
-    if (n_tiles > 1) issue(1);
-  } else {
-    issue(0);
-  }
-  wait_vmcnt<0>();
-  barrier_no_fence();
-
-  // ---- intervals. A wavefront's program is Q(0) P(0) Q(1) P(1) ... Q(n-1)
-  // P(n-1) [ ] P(n), where P(n) runs on a tile past the end (every score
-  // masked, so P(n) = 0) and only adds V(n-1)^T P(n-1)^T. Group A starts at
-  // interval 0, group B one interval later; both meet every barrier. In its
-  // Q-phase t (interval 2t for A, 2t+1 for B) a wavefront issues tile t + 2
-  // of K (group A) or tile t + 1 of V (group B): K(t) lands by interval 2t,
-  // V(t) by interval 2t + 1, two intervals after issue. Before each barrier
-  // a wavefront waits for its loads issued two or more intervals back.
-  const int lead = grp_b ? 1 : 2;
-  int since_issue = 2;   // intervals since this wavefront last issued loads
-  auto q_interval = [&](int t) __device__ {
-    const bool do_issue = t + lead < n_tiles;
-    if (do_issue) issue(t + lead);
-    if (t < n_tiles) q_phase(t);
-    since_issue = do_issue ? 0 : since_issue + 1;
-    if (since_issue == 0) wait_vmcnt<LPW>();
-    else wait_vmcnt<0>();
-    barrier_no_fence();
-  };
-  auto p_end = [&]() __device__ {
-    ++since_issue;
-    if (since_issue == 1) wait_vmcnt<LPW>();
-    else wait_vmcnt<0>();
-    barrier_no_fence();
-  };
-
-  if (grp_b) barrier_no_fence();   // B idles in interval 0
-  q_interval(0);
-  p_phase(false, 0, pf0, pf1);
-  p_end();
-  for (int t = 1; t <= n_tiles; t += 2) {
-    q_interval(t);
-    p_phase(true, t, pf1, pf0);
-    p_end();
-    if (t + 1 > n_tiles) break;
-    q_interval(t + 1);
-    p_phase(true, t + 1, pf0, pf1);
-    p_end();
-  }
-  if (!grp_b) barrier_no_fence();  // A idles in the last interval
-
-  // ---- epilogue: combine halves, normalise, write O and LSE
-  const float l_tot = pair_sum(l_run);
-  if (!q_ok) return;
-  float* op = p.o + it.b * p.o_sb + it.h * p.o_sh + (int64_t)qi * p.o_ss;
-  const bool empty = !(l_tot > 0.0f);
-  const float inv_l = empty ? 0.0f : 1.0f / l_tot;
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = db * 32 + 8 * g4 + 4 * hh;
-      f32x4 o4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o4[i] = acc[db][4 * g4 + i] * inv_l;
-      *reinterpret_cast<f32x4*>(op + d) = o4;
-    }
-  if (hh == 0) {
-    const float lse = empty ? kNegInf : m_run * p.scale + __logf(l_tot);
-    p.lse[it.b * p.lse_sb + it.h * p.lse_sh + qi] = lse;
-  }
+// Buffer descriptor over [base, base + rec) bytes, stride 0: loads past rec
+// return zeros.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int rec) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  i32x4 r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)((uint32_t)(a >> 32) & 0xFFFFu);
+  r[2] = rec;
+  r[3] = 0x00020000;
+  return r;
 }
 
-// ------------------------------- bf16 dense, one wavefront per SIMD, pipelined
+// LDS byte address of a shared-memory pointer.
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
+  return (uint32_t)(uintptr_t)(LDS_AS const unsigned char*)p;
+}
+
+// One 1-KiB load of a wavefront into LDS: lane l's 16 bytes at voffset land
+// at LDS address lds + 16 l. Issued from inline asm so that the compiler does
+// not track it: tracked, every control-flow join makes the compiler wait for
+// all such loads in flight before the next LDS read. The kernels order their
+// LDS reads after the data with an explicit s_waitcnt and a barrier.
+__device__ __forceinline__ void lds_dma16(uint32_t lds, uint32_t voffset, const i32x4& rsrc) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m0v), "v"(voffset), "s"(rsrc) : "memory");
+}
+
+// ------------------------------------ bf16, one wavefront per SIMD, pipelined
 //
 // Four wavefronts of 32 query rows each, one per SIMD. Each wavefront runs a
 // software pipeline over the key tiles, so that its own instruction stream
@@ -476,14 +203,16 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_bf16_pp_kernel(AttnParams
 //       row sum of x(t), the row max of S(t+1), the lazy-rescale decision and
 //       the scaling s c - m c of S(t+1).
 // Every query's arithmetic (product order, exp2 arguments, summation order,
-// rescale points, bf16 rounding of P) is the one of the other bf16 kernels,
-// so all of them give the same bits.
+// rescale points, bf16 rounding of P) depends on its own scores only, so
+// dense and block-sparse launches, any grid and any head chunking give the
+// same bits.
 //
 // K/V tiles go HBM -> LDS directly (buffer_load ... lds) into two slots per
 // tensor. Each slot is its own LDS variable and every access names its slot
 // at compile time (the step loop is unrolled by two), so the compiler can
-// tell the LDS reads of one slot from the loads in flight into the other and
-// does not make the reads wait for them. A step has two barriers: one after
+// tell the LDS reads of one slot from the loads in flight into the other;
+// the loads are issued from inline asm (lds_dma16), so control-flow joins do
+// not make the reads wait for them either. A step has two barriers: one after
 // phase 1 (all wavefronts are done with K(t+1)), one after phase 2 (done
 // with V(t)). Step t issues V(t+1) at its start, into the slot V(t-1) left,
 // and K(t+3) after its middle barrier, into the slot K(t+1) left; each load
@@ -564,25 +293,20 @@ __global__ __launch_bounds__(kSpWaves * 64, 1) void attn_fwd_bf16_sp_kernel(Attn
   }
   auto kslot = [&](int slot) __device__ -> unsigned char* { return slot ? lds_k1 : lds_k0; };
   auto vslot = [&](int slot) __device__ -> unsigned char* { return slot ? lds_v1 : lds_v0; };
+  // descriptors over the head's K and V rows (loads past the last key
+  // return zeros)
+  const i32x4 k_rsrc = make_rsrc(kp, k_rec), v_rsrc = make_rsrc(vp, v_rec);
   auto issue_k = [&](int t) __device__ {
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)kp, (short)0, k_rec, 0x00020000);
     const uint32_t base = (uint32_t)key0_of(t) * k_rb;
-    unsigned char* dst = kslot(t & 1) + wave * LPW * 1024;
+    const uint32_t dst = lds_addr(kslot(t & 1)) + wave * LPW * 1024;
 #pragma unroll
-    for (int j = 0; j < LPW; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(dst + j * 1024), 16,
-                                               (int)(koff[j] + base), 0, 0, 0);
+    for (int j = 0; j < LPW; ++j) lds_dma16(dst + j * 1024, koff[j] + base, k_rsrc);
   };
   auto issue_v = [&](int t) __device__ {
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)vp, (short)0, v_rec, 0x00020000);
     const uint32_t base = (uint32_t)key0_of(t) * v_rb;
-    unsigned char* dst = vslot(t & 1) + wave * LPW * 1024;
+    const uint32_t dst = lds_addr(vslot(t & 1)) + wave * LPW * 1024;
 #pragma unroll
-    for (int j = 0; j < LPW; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(dst + j * 1024), 16,
-                                               (int)(voff[j] + base), 0, 0, 0);
+    for (int j = 0; j < LPW; ++j) lds_dma16(dst + j * 1024, voff[j] + base, v_rsrc);
   };
 
   // ---- LDS fragment offsets inside a tile (per lane, loop-invariant). K
@@ -1004,19 +728,9 @@ hipError_t launch_attn_dense(const AttnParams& p0, DType dt, hipStream_t s) {
     hipLaunchKernelGGL((attn_fwd_f32_kernel<4, false>), dim3(p.n_items), dim3(256), 0, s, p);
     return hipGetLastError();
   }
-  // Grids of at least two 256-row workgroups per CU run the ping-pong
-  // kernel; smaller ones the one-wavefront-per-SIMD kernel, which keeps every
-  // SIMD busy with a single 128-row workgroup per CU. Both give the same bits.
-  const int64_t items_pp = (int64_t)p.B * p.H * ((p.Sq + 255) / 256);
-  if (items_pp >= 512) {
-    p.n_qblk = (p.Sq + 255) / 256;
-    p.n_items = p.B * p.H * p.n_qblk;
-    hipLaunchKernelGGL((attn_fwd_bf16_pp_kernel<8>), dim3(p.n_items), dim3(512), 0, s, p);
-  } else {
-    p.n_qblk = (p.Sq + kSpBM - 1) / kSpBM;
-    p.n_items = p.B * p.H * p.n_qblk;
-    hipLaunchKernelGGL(attn_fwd_bf16_sp_kernel<false>, dim3(p.n_items), dim3(kSpWaves * 64), 0, s, p);
-  }
+  p.n_qblk = (p.Sq + kSpBM - 1) / kSpBM;
+  p.n_items = p.B * p.H * p.n_qblk;
+  hipLaunchKernelGGL(attn_fwd_bf16_sp_kernel<false>, dim3(p.n_items), dim3(kSpWaves * 64), 0, s, p);
   return hipGetLastError();
 }
 
