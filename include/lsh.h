@@ -67,7 +67,14 @@ typedef enum lsh_dtype {
 
 typedef void* lsh_stream;   /* a hipStream_t */
 
-/* Arguments of one attention forward. */
+/*
+ * Arguments of one attention forward.
+ * Validation (before any HIP call): pointers 16-byte aligned, strides
+ * non-negative and multiples of 16 bytes, D = 128, B, Sq, Skv, H below
+ * 2^30, B*Sq*H below 2^31; for bf16, one head's K (and V) rows must span
+ * less than 2 GiB ((Skv - 1) * key stride * 2 + 256 bytes). Violations
+ * return LSH_ERR_INVALID or LSH_ERR_UNSUPPORTED.
+ */
 typedef struct lsh_attn_args {
   const void* q;          /* [B, Sq, H, D] elements of `dtype` */
   const void* k;          /* [B, Skv, H, D] */

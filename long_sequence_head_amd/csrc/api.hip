@@ -86,6 +86,15 @@ lsh_status validate_attn(const lsh_attn_args* a, bool allow_empty_kv, const char
   for (int i = 0; i < 5; ++i)
     if (ptrs[i] && !aligned16(ptrs[i]))
       return fail(LSH_ERR_INVALID, "%s: pointer %d is not 16-byte aligned", fn, i);
+  // bf16 K and V rows are read through buffer descriptors with 32-bit byte
+  // offsets: one head's rows must span less than 2 GiB.
+  if (a->dtype == LSH_BF16 && need_kv) {
+    const int64_t span_k = (a->Skv - 1) * a->k_stride[1] * eb + a->D * eb;
+    const int64_t span_v = (a->Skv - 1) * a->v_stride[1] * eb + a->D * eb;
+    if (span_k >= ((int64_t)1 << 31) || span_v >= ((int64_t)1 << 31))
+      return fail(LSH_ERR_UNSUPPORTED,
+                  "%s: the K/V rows of one head span 2 GiB or more (Skv x key stride)", fn);
+  }
   const int64_t* strides[4] = {a->q_stride, a->k_stride, a->v_stride, a->o_stride};
   const int ebs[4] = {eb, eb, eb, 4};
   for (int t = 0; t < 4; ++t) {

@@ -90,6 +90,9 @@ BAD_CASES = [
     ("negative stride", lambda a: a.k_stride.__setitem__(2, -128), _lib.LSH_ERR_INVALID),
     ("nan scale", lambda a: setattr(a, "scale", float("nan")), _lib.LSH_ERR_INVALID),
     ("huge S", lambda a: setattr(a, "Sq", 1 << 31), _lib.LSH_ERR_UNSUPPORTED),
+    # 2^20 keys x a 2048-element key stride x 2 bytes = 4 GiB of one head's rows
+    ("K span over 2 GiB", lambda a: (setattr(a, "Skv", 1 << 20), a.k_stride.__setitem__(1, 2048)),
+     _lib.LSH_ERR_UNSUPPORTED),
 ]
 
 
