@@ -1,16 +1,16 @@
 #!/usr/bin/env python3
 """Attention forward throughput on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads 4,3,2,5]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads 4,3,2,5,1]
 
 Headline (the JSON line's `value`): dense non-causal bf16 attention,
 B=1, S=56160, H=40, D=128, fp32 O + LSE, algorithmic TFLOP/s =
 4*B*H*S*S*D / time. One step = one lsh_attn_fwd over the whole input.
 Secondary workloads (same line, under "workloads"): the head-chunked
 two-stream pipeline at S=32760 ({16,12,12} chunks, permute included), the
-ring partials + LSE merge (Q 4096 tokens, 8 KV blocks of 4096, H=8) and
-the block-sparse workload (S=32768, 128x128 mask, per-head density
-U[0.1,0.6)). Inputs are the seeded synthetic tensors of lsh_inputs,
+ring partials + LSE merge (Q 4096 tokens, 8 KV blocks of 4096, H=8), the
+block-sparse workload (S=32768, 128x128 mask, per-head density
+U[0.1,0.6)) and the small fp32 case (B=4, S=128, H=32). Inputs are the seeded synthetic tensors of lsh_inputs,
 resident in HBM before timing. `cpu_baseline` times the fp64 oracle on a
 bounded sample of the headline workload on the host cores.
 """
@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s and % bf16 MFMA peak at S=32K/56K, 1 MI355X"
 PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
+PEAK_F32_MATRIX_TFLOPS = 157.3   # MI355X dense fp32 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_S56160_H40_traffic.json")
 KERNEL_SOURCES = ["long_sequence_head_amd/csrc/attn_fwd.hip",
                   "long_sequence_head_amd/csrc/lsh_internal.hpp"]
@@ -90,8 +91,11 @@ def bench_dense(L, I, w, steps, warmup):
     ms, wall = timed(lambda: L.attn_fwd(qg, kg, vg, o=o, lse=lse), steps, warmup)
     flops = 4 * w.B * w.H * w.Sq * w.Skv * w.D
     tf = flops / ms / 1e9
-    log(f"[bench] workload {w.wid}: {ms:.3f} ms/step, {tf:.1f} TFLOP/s ({100 * tf / PEAK_BF16_TFLOPS:.1f}% of peak)")
-    return dict(ms=ms, wall_ms=wall, tflops=tf, flops=flops), (q, k, v, o, lse)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MATRIX_TFLOPS
+    log(f"[bench] workload {w.wid}: {ms:.3f} ms/step, {tf:.1f} TFLOP/s ({100 * tf / peak:.1f}% of the "
+        f"{w.dtype} matrix peak)")
+    return dict(ms=ms, wall_ms=wall, tflops=tf, flops=flops, pct_of_matrix_peak=100 * tf / peak,
+                matrix_peak_tflops=peak), (q, k, v, o, lse)
 
 
 def bench_chunked(L, I, w, steps, warmup):
@@ -254,7 +258,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workloads", default="4,3,2,5",
+    ap.add_argument("--workloads", default="4,3,2,5,1",
                     help="comma list; 4 (the headline) is always run")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the CPU oracle sample (0 disables)")

@@ -223,6 +223,25 @@ def test_partial_and_merge_small(L, dtype):
             tol_o=1e-5, tol_lse=1e-5)
 
 
+@pytest.mark.parametrize("n", [1, 8, 9, 17])
+def test_merge_counts_vs_oracle(L, n):
+    """n partials (one, exactly one group of 8, and counts that leave a
+    partial group) with random outputs and LSEs, some -inf: GPU merge vs the
+    oracle merge of the same values."""
+    G.announce(f"merge n={n}")
+    t = G.torch()
+    B, Sq, H, D = 2, 37, 3, 128
+    rng = np.random.default_rng(500 + n)
+    o_parts = rng.standard_normal((n, B, Sq, H, D)).astype(np.float32)
+    l_parts = (rng.standard_normal((n, B, H, Sq)) * 4).astype(np.float32)
+    l_parts[rng.random(l_parts.shape) < 0.2] = -np.inf
+    o_parts[np.broadcast_to(np.isneginf(l_parts).transpose(0, 1, 3, 2)[..., None], o_parts.shape)] = 0
+    o, lse = L.lse_merge(t.from_numpy(o_parts).cuda(), t.from_numpy(l_parts).cuda())
+    om, lm = oracle.merge_ref(o_parts, l_parts)
+    G.check(f"merge n={n}", "f32", o.cpu().numpy(), lse.cpu().numpy(), om, lm,
+            tol_o=1e-5, tol_lse=1e-5)
+
+
 def test_merge_all_empty(L):
     G.announce("merge all empty")
     t = G.torch()
