@@ -9,7 +9,8 @@ the operation written out, with no blocking beyond independent query-row
 blocks, no fusion and no reordering of the mathematics.
 """
 from .attention import (attention_ref, merge_ref, permute_ref,
-                        inverse_permute_ref, attention_flops)
+                        inverse_permute_ref, attention_flops, attention_bwd_ref,
+                        attention_bwd_flops)
 
 __all__ = ["attention_ref", "merge_ref", "permute_ref", "inverse_permute_ref",
-           "attention_flops"]
+           "attention_flops", "attention_bwd_ref", "attention_bwd_flops"]

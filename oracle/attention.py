@@ -162,3 +162,78 @@ def permute_ref(x, h0, hc):
 def inverse_permute_ref(y):
     """[B, hc, S, D] -> [B, S, hc, D]."""
     return np.ascontiguousarray(np.asarray(y).transpose(0, 2, 1, 3))
+
+
+def attention_bwd_ref(q, k, v, dout, scale, rows=None, keys=None, heads=None):
+    """Gradients of dense softmax attention, in float64.
+
+    The forward is attention_ref without a mask: O = P V with
+    P = softmax_j(scale * <q_i, k_j>). For a loss L with dL/dO = dout
+    (called dO below), the chain rule gives, per batch entry and head:
+
+        dV = P^T dO
+        dP = dO V^T
+        dS = P * (dP - rowsum(P * dP))      (softmax Jacobian, row by row)
+        dQ = scale * dS K
+        dK = scale * dS^T Q
+
+    The CHARM+ pages ("CHARM+: How Cross-Hardware Attention Breaks Through
+    Distributed Communication Bottlenecks", section "Measured Speedups")
+    report the backward pass beside the forward; the pages give no
+    formulas, so this is the plain derivative of the forward they define.
+
+    q, dout: [B, Sq, H, D]; k, v: [B, Skv, H, D]; any real dtype.
+    rows: optional query indices for dQ; keys: optional key indices for dK
+    and dV (the other outputs are computed over all rows / keys as the
+    definition requires). heads: optional head indices; others stay NaN.
+    Returns dQ [B, R, H, D], dK [B, K, H, D], dV [B, K, H, D] (float64).
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    dout = np.asarray(dout)
+    B, Sq, H, D = q.shape
+    Skv = k.shape[1]
+    if k.shape != (B, Skv, H, D) or v.shape != k.shape or dout.shape != q.shape:
+        raise ValueError("q, k, v, dout shapes disagree")
+    rows = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
+    keys = np.arange(Skv) if keys is None else np.asarray(keys, dtype=np.int64)
+    heads = range(H) if heads is None else list(heads)
+    dq = np.full((B, rows.size, H, D), np.nan)
+    dk = np.full((B, keys.size, H, D), np.nan)
+    dv = np.full((B, keys.size, H, D), np.nan)
+    row_pos = {int(r): i for i, r in enumerate(rows)}
+    for b in range(B):
+        for h in heads:
+            kh = k[b, :, h, :].astype(np.float64)
+            vh = v[b, :, h, :].astype(np.float64)
+            kk = kh[keys]
+            dk_acc = np.zeros((keys.size, D))
+            dv_acc = np.zeros((keys.size, D))
+            for r0 in range(0, Sq, _ROW_BLOCK):
+                idx = np.arange(r0, min(Sq, r0 + _ROW_BLOCK))
+                qh = q[b, idx, h, :].astype(np.float64)
+                doh = dout[b, idx, h, :].astype(np.float64)
+                s = (qh @ kh.T) * float(scale)                 # [r, Skv]
+                m = s.max(axis=1, keepdims=True)
+                e = np.exp(s - m)
+                p = e / e.sum(axis=1, keepdims=True)             # softmax over keys
+                dp = doh @ vh.T                                  # [r, Skv]
+                ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+                dv_acc += p[:, keys].T @ doh
+                dk_acc += float(scale) * ds[:, keys].T @ qh
+                sel = [i for i, r in enumerate(idx) if int(r) in row_pos]
+                if sel:
+                    dq_blk = float(scale) * ds[sel] @ kh
+                    for j, i in enumerate(sel):
+                        dq[b, row_pos[int(idx[i])], h, :] = dq_blk[j]
+            dk[b, :, h, :] = dk_acc
+            dv[b, :, h, :] = dv_acc
+    return dq, dk, dv
+
+
+def attention_bwd_flops(B, H, Sq, Skv, D) -> int:
+    """Algorithmic flop count of one attention backward: the five products
+    S = Q K^T, dV = P^T dO, dP = dO V^T, dQ = dS K and dK = dS^T Q, each
+    2*Sq*Skv*D flops, per batch entry and head."""
+    return 10 * B * H * Sq * Skv * D

@@ -381,3 +381,96 @@ ATTN_PINS = [pin_constant_v, pin_identical_keys, pin_single_key, pin_zero_query,
              pin_head_partition_tp_demo, pin_key_permutation, pin_key_shift,
              pin_mask_all_ones, pin_mask_diagonal, pin_mask_gather, pin_row_subset]
 MERGE_PINS = [pin_merge_split, pin_merge_closed_forms]
+
+
+# ------------------------------------------------------------------ backward
+#
+# Pins of the gradient oracle (signature of ``oracle.attention_bwd_ref``).
+# The first differentiates the forward oracle numerically, so it pins the
+# gradient to the forward definition without using the gradient formulas;
+# the others are exact consequences of the softmax Jacobian.
+
+def _bwd_case(seed, B=2, Sq=3, Skv=4, H=2, D=5):
+    r = _rng(seed)
+    return (r.standard_normal((B, Sq, H, D)), r.standard_normal((B, Skv, H, D)),
+            r.standard_normal((B, Skv, H, D)), r.standard_normal((B, Sq, H, D)))
+
+
+def pin_bwd_finite_differences(bwd, attn):
+    """Central differences of L = sum(dO * O(q, k, v)) in float64 match
+    every entry of dQ, dK and dV (step 1e-6: truncation ~1e-12, rounding
+    ~1e-10)."""
+    scale = 0.7
+    q, k, v, do = _bwd_case(201)
+    dq, dk, dv = bwd(q, k, v, do, scale)
+
+    def loss(q_, k_, v_):
+        o, _ = attn(q_, k_, v_, scale)
+        return float((do * o).sum())
+
+    eps = 1e-6
+    for name, x, g in (("dQ", q, dq), ("dK", k, dk), ("dV", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = x.copy(); xp[idx] += eps
+            xm = x.copy(); xm[idx] -= eps
+            args_p = {"dQ": (xp, k, v), "dK": (q, xp, v), "dV": (q, k, xp)}[name]
+            args_m = {"dQ": (xm, k, v), "dK": (q, xm, v), "dV": (q, k, xm)}[name]
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        _close(g, num, tol=1e-7, what=f"finite differences {name}")
+
+
+def pin_bwd_column_sums(bwd, attn=None):
+    """Each row of dS sums to zero, so sum_j dK_j = 0; each row of P sums
+    to one, so sum_j dV_j = sum_i dO_i (per batch entry and head)."""
+    q, k, v, do = _bwd_case(202, B=2, Sq=9, Skv=13, H=3, D=6)
+    dq, dk, dv = bwd(q, k, v, do, 0.45)
+    _close(dk.sum(axis=1), np.zeros_like(dk.sum(axis=1)), tol=1e-12, what="sum dK")
+    _close(dv.sum(axis=1), do.sum(axis=1), tol=1e-12, what="sum dV")
+
+
+def pin_bwd_identical_keys(bwd, attn=None):
+    """All keys equal: scores are constant along each row, P is uniform and
+    dQ = scale * dS K = scale * (sum_j dS_ij) kappa = 0."""
+    q, k, v, do = _bwd_case(203, B=1, Sq=6, Skv=7, H=2, D=4)
+    k[:] = _rng(9).standard_normal(4)
+    dq, dk, dv = bwd(q, k, v, do, 0.9)
+    _close(dq, np.zeros_like(dq), tol=1e-12, what="dQ with identical keys")
+    _close(dv, np.broadcast_to(do.sum(axis=1, keepdims=True) / 7, dv.shape), tol=1e-12,
+           what="dV with identical keys")
+
+
+def pin_bwd_single_key(bwd, attn=None):
+    """One key: P = 1, dS = 0, so dQ = dK = 0 and dV_0 = sum_i dO_i."""
+    q, k, v, do = _bwd_case(204, B=2, Sq=5, Skv=1, H=2, D=3)
+    dq, dk, dv = bwd(q, k, v, do, 1.3)
+    _close(dq, np.zeros_like(dq), what="dQ one key")
+    _close(dk, np.zeros_like(dk), what="dK one key")
+    _close(dv, do.sum(axis=1, keepdims=True), what="dV one key")
+
+
+def pin_bwd_zero_scale(bwd, attn=None):
+    """scale = 0: P uniform (1/Skv), dQ = dK = 0 (both carry the factor
+    scale) and every dV_j = (1/Skv) sum_i dO_i."""
+    q, k, v, do = _bwd_case(205, B=1, Sq=4, Skv=6, H=2, D=5)
+    dq, dk, dv = bwd(q, k, v, do, 0.0)
+    _close(dq, np.zeros_like(dq), what="dQ scale 0")
+    _close(dk, np.zeros_like(dk), what="dK scale 0")
+    _close(dv, np.broadcast_to(do.sum(axis=1, keepdims=True) / 6, dv.shape), what="dV scale 0")
+
+
+def pin_bwd_subsets(bwd, attn=None):
+    """Computing selected query rows (dQ) and keys (dK, dV) equals the same
+    entries of the full run."""
+    q, k, v, do = _bwd_case(206, B=1, Sq=300, Skv=37, H=2, D=4)
+    dq, dk, dv = bwd(q, k, v, do, 0.5)
+    rows = np.array([0, 7, 256, 299])
+    keys = np.array([3, 36])
+    dq2, dk2, dv2 = bwd(q, k, v, do, 0.5, rows=rows, keys=keys)
+    _close(dq2, dq[:, rows], what="dQ rows")
+    _close(dk2, dk[:, keys], what="dK keys")
+    _close(dv2, dv[:, keys], what="dV keys")
+
+
+BWD_PINS = [pin_bwd_finite_differences, pin_bwd_column_sums, pin_bwd_identical_keys,
+            pin_bwd_single_key, pin_bwd_zero_scale, pin_bwd_subsets]

@@ -17,6 +17,11 @@ def test_merge_pin(pin):
     pin(oracle.attention_ref, oracle.merge_ref)
 
 
+@pytest.mark.parametrize("pin", P.BWD_PINS, ids=lambda f: f.__name__)
+def test_backward_pin(pin):
+    pin(oracle.attention_bwd_ref, oracle.attention_ref)
+
+
 def test_permute_indexwise():
     """dst[b, h-h0, s, :] == src[b, s, h, :], checked element by element."""
     r = np.random.default_rng(0)

@@ -112,3 +112,63 @@ def test_attention_mutant_is_caught(name):
 @pytest.mark.parametrize("name", sorted(MERGE_MUTANTS))
 def test_merge_mutant_is_caught(name):
     assert _fails_some_pin(oracle.attention_ref, MERGE_MUTANTS[name], P.MERGE_PINS), name
+
+
+# ------------------------------------------------------------------ backward
+
+def _bwd_mutant(kind):
+    """A gradient implementation with one planted mistake."""
+    def bwd(q, k, v, do, scale, rows=None, keys=None, heads=None):
+        q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+        B, Sq, H, D = q.shape
+        dq = np.zeros_like(q)
+        dk = np.zeros_like(k)
+        dv = np.zeros_like(v)
+        for b in range(B):
+            for h in range(H):
+                qh, kh, vh, doh = q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h]
+                s = scale * qh @ kh.T
+                e = np.exp(s - s.max(axis=1, keepdims=True))
+                p = e if kind == "p_unnormalised" else e / e.sum(axis=1, keepdims=True)
+                dp = doh @ vh.T
+                delta = (p * dp).sum(axis=1, keepdims=True)
+                if kind == "no_delta":
+                    ds = p * dp
+                elif kind == "delta_sign":
+                    ds = p * (dp + delta)
+                else:
+                    ds = p * (dp - delta)
+                dq[b, :, h] = (1.0 if kind == "dq_no_scale" else scale) * ds @ (
+                    vh if kind == "dq_uses_v" else kh)
+                dk[b, :, h] = scale * ds.T @ (doh if kind == "dk_uses_do" else qh)
+                dv[b, :, h] = (ds if kind == "dv_uses_ds" else p).T @ doh
+        if rows is not None:
+            dq = dq[:, np.asarray(rows)]
+        if keys is not None:
+            dk, dv = dk[:, np.asarray(keys)], dv[:, np.asarray(keys)]
+        return dq, dk, dv
+    return bwd
+
+
+BWD_MUTANTS = ["no_delta", "delta_sign", "dq_no_scale", "dq_uses_v", "dk_uses_do",
+               "dv_uses_ds", "p_unnormalised"]
+
+
+def test_backward_mutant_helper_is_faithful():
+    """Without a planted mistake the helper passes every pin, so a failing
+    mutant fails because of its mistake."""
+    for pin in P.BWD_PINS:
+        pin(_bwd_mutant("none"), oracle.attention_ref)
+
+
+@pytest.mark.parametrize("kind", BWD_MUTANTS)
+def test_backward_mutant_is_caught(kind):
+    bwd = _bwd_mutant(kind)
+    caught = False
+    for pin in P.BWD_PINS:
+        try:
+            pin(bwd, oracle.attention_ref)
+        except AssertionError:
+            caught = True
+            break
+    assert caught, f"no pin catches backward mutant {kind}"
