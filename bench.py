@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Attention forward throughput on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads 4,3,2,5,1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads 4,3,2,5,1,6]
 
 Headline (the JSON line's `value`): dense non-causal bf16 attention,
 B=1, S=56160, H=40, D=128, fp32 O + LSE, algorithmic TFLOP/s =
@@ -10,8 +10,9 @@ Secondary workloads (same line, under "workloads"): the head-chunked
 two-stream pipeline at S=32760 ({16,12,12} chunks, permute included), the
 ring partials + LSE merge (Q 4096 tokens, 8 KV blocks of 4096, H=8), the
 block-sparse workload (S=32768, 128x128 mask, per-head density
-U[0.1,0.6)) and the small fp32 case (B=4, S=128, H=32). Inputs are the seeded synthetic tensors of lsh_inputs,
-resident in HBM before timing. `cpu_baseline` times the fp64 oracle on a
+U[0.1,0.6)), the small fp32 case (B=4, S=128, H=32) and the backward
+(dQ, dK, dV) of the dense forward at S=32760, H=40. Inputs are the seeded
+synthetic tensors of lsh_inputs, resident in HBM before timing. `cpu_baseline` times the fp64 oracle on a
 bounded sample of the headline workload on the host cores.
 """
 from __future__ import annotations
@@ -33,6 +34,7 @@ PEAK_HBM_GBS = 8000.0
 PEAK_F32_MATRIX_TFLOPS = 157.3   # MI355X dense fp32 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_S56160_H40_traffic.json")
 KERNEL_SOURCES = ["long_sequence_head_amd/csrc/attn_fwd.hip",
+                  "long_sequence_head_amd/csrc/attn_common.hpp",
                   "long_sequence_head_amd/csrc/lsh_internal.hpp"]
 
 
@@ -199,6 +201,36 @@ def bench_sparse(L, I, w, steps, warmup):
 
 # ---------------------------------------------------------------- CPU oracle
 
+def bench_bwd(L, I, w, steps, warmup):
+    """Backward of the dense forward: one step = one lsh_attn_bwd (row
+    statistics, dK/dV and dQ kernels) on resident Q, K, V, dO, O, LSE.
+    Algorithmic flops 10*B*H*Sq*Skv*D (dV, dP, dQ, dK: 2 each, plus the
+    recomputed S); the kernels issue 14*B*H*Sq*Skv*D of matrix work, since
+    S and dP are formed in both the dK/dV and the dQ pass."""
+    import torch
+    log(f"[bench] workload {w.wid}: {w.name}: generating inputs")
+    q, k, v = I.make_qkv(w, seed=0)
+    do = I.make_dout(w, seed=0)
+    qg, kg, vg, dog = (upload(x, w.dtype) for x in (q, k, v, do))
+    del q, k, v, do
+    o, lse = L.attn_fwd(qg, kg, vg)
+    dq = torch.empty((w.B, w.Sq, w.H, w.D), dtype=torch.float32, device="cuda")
+    dk = torch.empty((w.B, w.Skv, w.H, w.D), dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+    ws = torch.empty(L.bwd_workspace_bytes(qg, kg, vg) + 256, dtype=torch.uint8, device="cuda")
+    ms, wall = timed(lambda: L.attn_bwd(qg, kg, vg, dog, o, lse, dq=dq, dk=dk, dv=dv, workspace=ws),
+                     steps, warmup)
+    flops = 10 * w.B * w.H * w.Sq * w.Skv * w.D
+    issued = 14 * w.B * w.H * w.Sq * w.Skv * w.D
+    r = dict(ms=ms, wall_ms=wall, tflops=flops / ms / 1e9, flops=flops,
+             issued_matrix_tflops=issued / ms / 1e9,
+             pct_of_bf16_peak=100 * flops / ms / 1e9 / PEAK_BF16_TFLOPS)
+    log(f"[bench] workload {w.wid}: {ms:.3f} ms/step, {r['tflops']:.1f} TFLOP/s algorithmic "
+        f"({r['pct_of_bf16_peak']:.1f}% of the bf16 peak), {r['issued_matrix_tflops']:.1f} TFLOP/s "
+        "of issued matrix work")
+    return r
+
+
 def cpu_baseline(I, w, q, k, v, o_gpu, lse_gpu, target_s):
     """Times the fp64 oracle on query rows 0..n-1 of head 0 against all keys,
     with n grown until the run takes about `target_s` seconds."""
@@ -258,7 +290,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workloads", default="4,3,2,5,1",
+    ap.add_argument("--workloads", default="4,3,2,5,1,6",
                     help="comma list; 4 (the headline) is always run")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the CPU oracle sample (0 disables)")
@@ -310,6 +342,8 @@ def main():
         elif wid == 1:
             r, _ = bench_dense(L, I, w, args.steps, args.warmup)
             secondary[w.name] = r
+        elif wid == 6:
+            secondary[w.name] = bench_bwd(L, I, w, args.steps, args.warmup)
         torch.cuda.empty_cache()
 
     ms = head["ms"]

@@ -1,6 +1,6 @@
 /*
- * lsh.h - exact long-sequence multi-head attention forward for AMD MI355X
- * (gfx950). C ABI of liblsh.so.
+ * lsh.h - exact long-sequence multi-head attention (forward and backward)
+ * for AMD MI355X (gfx950). C ABI of liblsh.so.
  *
  * What the library computes. For every batch entry b and head h, with
  * scores s_ij = scale * <q_i, k_j>, the forward pass of softmax attention
@@ -12,11 +12,13 @@
  * interact). O is returned in float32, LSE in float32. The computation is
  * exact up to floating-point rounding: a blockwise online softmax over key
  * tiles of 64, with QK^T and PV on the matrix cores and fp32 accumulation.
+ * lsh_attn_bwd gives the gradients of the dense forward (see there).
  *
  * Conventions shared by every entry point.
  *  - Pointers named q, k, v, o, lse, src, dst, o_parts, lse_parts,
- *    block_mask and workspace are DEVICE pointers owned by the caller. The
- *    library allocates no device memory and keeps no per-call state.
+ *    block_mask, dout, dq, dk, dv and workspace are DEVICE pointers owned
+ *    by the caller. The library allocates no device memory and keeps no
+ *    per-call state.
  *  - Streams are hipStream_t values passed as void*; NULL is the null
  *    stream. Every function only enqueues work and returns; results are
  *    ready when the stream(s) reach that point.
@@ -205,6 +207,62 @@ lsh_status lsh_attn_fwd_blocksparse(const lsh_attn_args* args,
 
 /* Workspace bytes of lsh_attn_fwd_blocksparse. 0 on bad args. */
 size_t lsh_attn_fwd_blocksparse_workspace(const lsh_attn_args* args);
+
+/*
+ * Arguments of one attention backward (bf16 only).
+ * The forward is lsh_attn_fwd on the same q, k, v and scale; o and lse
+ * are its outputs. Validation (before any HIP call) as for
+ * lsh_attn_args; in addition dtype must be LSH_BF16 (LSH_F32 returns
+ * LSH_ERR_UNSUPPORTED), and one head's Q (and dO) rows must span less
+ * than 2 GiB, like K and V.
+ */
+typedef struct lsh_attn_bwd_args {
+  const void* q;          /* bf16 [B, Sq, H, D] */
+  const void* k;          /* bf16 [B, Skv, H, D] */
+  const void* v;          /* bf16 [B, Skv, H, D] */
+  const void* dout;       /* bf16 [B, Sq, H, D]: gradient of the loss w.r.t. O */
+  const float* o;         /* float32 [B, Sq, H, D]: the forward's O */
+  const float* lse;       /* float32 [B, H, Sq], contiguous: the forward's LSE */
+  float* dq;              /* float32 [B, Sq, H, D] */
+  float* dk;              /* float32 [B, Skv, H, D] */
+  float* dv;              /* float32 [B, Skv, H, D] */
+  int32_t dtype;          /* lsh_dtype; only LSH_BF16 */
+  int32_t reserved;       /* must be 0 */
+  int64_t B, Sq, Skv, H, D;
+  int64_t q_stride[3];    /* element strides of (b, s, h) */
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t do_stride[3];
+  int64_t o_stride[3];
+  int64_t dq_stride[3];
+  int64_t dk_stride[3];
+  int64_t dv_stride[3];
+  float scale;            /* the forward's score multiplier */
+} lsh_attn_bwd_args;
+
+/*
+ * Attention backward: gradients of the dense forward (lsh_attn_fwd) with
+ * respect to q, k and v for a loss whose gradient with respect to O is
+ * dout. With P = exp(scale q k^T - LSE) per (b, h):
+ *   dV = P^T dO,   dP = dO V^T,   Delta = rowsum(dO * O),
+ *   dS = P * (dP - Delta),   dQ = scale dS K,   dK = scale dS^T Q.
+ * Source: the forward's definition (the TP page above, sections 2-3)
+ * differentiated; CHARM+ ("CHARM+: How Cross-Hardware Attention Breaks
+ * Through Distributed Communication Bottlenecks", section "Measured
+ * Speedups") reports the backward pass beside the forward.
+ * dQ, dK, dV are written in float32 (every element, no accumulation into
+ * prior contents). Skv >= 1. Deterministic: no atomics; dK/dV and dQ come
+ * from separate kernels that each rebuild P.
+ * workspace: device memory of at least lsh_attn_bwd_workspace(args)
+ * bytes, 256-byte aligned (per-row LSE * log2(e) and Delta); same reuse
+ * rule as the chunked workspace.
+ */
+lsh_status lsh_attn_bwd(const lsh_attn_bwd_args* args, void* workspace,
+                        size_t workspace_bytes, lsh_stream stream);
+
+/* Workspace bytes of lsh_attn_bwd: B * H * ceil(Sq / 64) * 512. 0 on bad
+ * args. */
+size_t lsh_attn_bwd_workspace(const lsh_attn_bwd_args* args);
 
 #ifdef __cplusplus
 }

@@ -1,4 +1,4 @@
-"""Exact long-sequence multi-head attention forward on MI355X (gfx950).
+"""Exact long-sequence multi-head attention on MI355X (gfx950).
 
 Python binding of liblsh.so (include/lsh.h). It only marshals arguments:
 every step runs in the library's HIP kernels. PyTorch provides device
@@ -15,6 +15,7 @@ Functions:
   lse_merge           merge of per-block partial results
   head_permute        [B, S, H, D] -> [B, hc, S, D] copy of heads [h0, h0+hc)
   attn_fwd_blocksparse  attention restricted to a 128x128 block mask
+  attn_bwd            gradients dQ, dK, dV of the dense forward (bf16)
 """
 from __future__ import annotations
 
@@ -25,7 +26,8 @@ from . import _lib
 from ._lib import LshError, load  # noqa: F401
 
 __all__ = ["attn_fwd", "attn_fwd_chunked", "attn_partial", "lse_merge", "head_permute",
-           "attn_fwd_blocksparse", "chunked_workspace_bytes", "blocksparse_workspace_bytes",
+           "attn_fwd_blocksparse", "attn_bwd", "bwd_workspace_bytes",
+           "chunked_workspace_bytes", "blocksparse_workspace_bytes",
            "LshError", "load", "MASK_BLOCK"]
 
 MASK_BLOCK = 128
@@ -256,3 +258,67 @@ def attn_fwd_blocksparse(q, k, v, block_mask, scale=None, o=None, lse=None, work
                                       _stream_ptr(stream))
     _lib.check("lsh_attn_fwd_blocksparse", st)
     return o, lse
+
+
+def _bwd_args(q, k, v, dout, o, lse, dq, dk, dv, scale):
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _check4(name, t)
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16 (the backward supports bf16 only)")
+    B, Sq, H, D = q.shape
+    Skv = k.shape[1]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != H or k.shape[3] != D:
+        raise ValueError(f"k/v shape {tuple(k.shape)}/{tuple(v.shape)} does not match q {tuple(q.shape)}")
+    if dout.shape != q.shape:
+        raise ValueError("dout must have the shape of q")
+    for name, t, shape in (("o", o, q.shape), ("dq", dq, q.shape), ("dk", dk, k.shape),
+                           ("dv", dv, k.shape)):
+        if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or t.stride(-1) != 1:
+            raise ValueError(f"{name} must be float32 {tuple(shape)} with contiguous head_dim")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Sq) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, Sq]")
+    a = _lib.AttnBwdArgs()
+    a.q, a.k, a.v, a.dout = q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr()
+    a.o, a.lse = o.data_ptr(), lse.data_ptr()
+    a.dq, a.dk, a.dv = dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    a.dtype, a.reserved = _lib.LSH_BF16, 0
+    a.B, a.Sq, a.Skv, a.H, a.D = B, Sq, Skv, H, D
+    for field, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("do_stride", dout),
+                     ("o_stride", o), ("dq_stride", dq), ("dk_stride", dk), ("dv_stride", dv)):
+        getattr(a, field)[:] = [t.stride(0), t.stride(1), t.stride(2)]
+    a.scale = float(1.0 / math.sqrt(D) if scale is None else scale)
+    return a
+
+
+def bwd_workspace_bytes(q, k, v):
+    """Workspace bytes lsh_attn_bwd needs for these shapes: the header's
+    B * H * ceil(Sq / 64) * 512 (lsh_attn_bwd_workspace)."""
+    B, Sq, H, _ = q.shape
+    return B * H * (-(-Sq // 64)) * 512
+
+
+def attn_bwd(q, k, v, dout, o, lse, scale=None, dq=None, dk=None, dv=None, workspace=None,
+             stream=None):
+    """Gradients of the dense forward: q, k, v, dout bfloat16 [B, S, H, D];
+    o and lse the forward's float32 outputs. Returns (dQ, dK, dV) float32."""
+    lib = load()
+    torch = _torch()
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    a = _bwd_args(q, k, v, dout, o, lse, dq, dk, dv, scale)
+    need = int(lib.lsh_attn_bwd_workspace(ctypes.byref(a)))
+    if need == 0:
+        _lib.check("lsh_attn_bwd_workspace", _lib.LSH_ERR_INVALID)
+    if workspace is None:
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
+    base = workspace.data_ptr()
+    aligned = (base + 255) // 256 * 256
+    st = lib.lsh_attn_bwd(ctypes.byref(a), ctypes.c_void_p(aligned),
+                          workspace.numel() - (aligned - base), _stream_ptr(stream))
+    _lib.check("lsh_attn_bwd", st)
+    return dq, dk, dv

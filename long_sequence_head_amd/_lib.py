@@ -29,7 +29,21 @@ class AttnArgs(ctypes.Structure):
     ]
 
 
+class AttnBwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("q", c_vp), ("k", c_vp), ("v", c_vp), ("dout", c_vp), ("o", c_vp), ("lse", c_vp),
+        ("dq", c_vp), ("dk", c_vp), ("dv", c_vp),
+        ("dtype", c_i32), ("reserved", c_i32),
+        ("B", c_i64), ("Sq", c_i64), ("Skv", c_i64), ("H", c_i64), ("D", c_i64),
+        ("q_stride", c_i64 * 3), ("k_stride", c_i64 * 3), ("v_stride", c_i64 * 3),
+        ("do_stride", c_i64 * 3), ("o_stride", c_i64 * 3), ("dq_stride", c_i64 * 3),
+        ("dk_stride", c_i64 * 3), ("dv_stride", c_i64 * 3),
+        ("scale", ctypes.c_float),
+    ]
+
+
 _ARGS_P = ctypes.POINTER(AttnArgs)
+_BWD_P = ctypes.POINTER(AttnBwdArgs)
 SIGNATURES = {
     "lsh_abi_version": (ctypes.c_int, []),
     "lsh_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -44,6 +58,8 @@ SIGNATURES = {
     "lsh_head_permute": (ctypes.c_int, [c_vp, c_vp, c_i32, c_i64, c_i64, c_i64, c_i64, c_i32, c_i32, c_vp]),
     "lsh_attn_fwd_blocksparse": (ctypes.c_int, [_ARGS_P, c_vp, c_vp, ctypes.c_size_t, c_vp]),
     "lsh_attn_fwd_blocksparse_workspace": (ctypes.c_size_t, [_ARGS_P]),
+    "lsh_attn_bwd": (ctypes.c_int, [_BWD_P, c_vp, ctypes.c_size_t, c_vp]),
+    "lsh_attn_bwd_workspace": (ctypes.c_size_t, [_BWD_P]),
 }
 
 _lock = threading.Lock()

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIBNAME = "liblsh.so"
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["attn_fwd.hip", "aux_kernels.hip", "api.hip"]
+SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "aux_kernels.hip", "api.hip"]
 # Per-file code generation options. The attention kernels keep their MFMA
 # accumulators in VGPRs: the scores feed VALU work directly and the register
 # allocator otherwise shuttles them through AGPRs.

@@ -1,6 +1,6 @@
 // C ABI of liblsh.so: argument validation, launch set-up and the
-// two-stream head-chunk pipeline. Kernels live in attn_fwd.hip and
-// aux_kernels.hip.
+// two-stream head-chunk pipeline. Kernels live in attn_fwd.hip,
+// attn_bwd.hip and aux_kernels.hip.
 #include "lsh.h"
 #include "lsh_internal.hpp"
 
@@ -138,6 +138,89 @@ lsh::AttnParams make_params(const lsh_attn_args* a) {
   p.Skv = (int32_t)a->Skv;
   p.scale = a->scale;
   p.scale_log2 = (float)((double)a->scale * 1.4426950408889634);  // scale * log2(e)
+  return p;
+}
+
+// Validates a backward argument block (no HIP call).
+lsh_status validate_bwd(const lsh_attn_bwd_args* a, const char* fn) {
+  if (!a) return fail(LSH_ERR_INVALID, "%s: args is NULL", fn);
+  if (a->dtype != LSH_F32 && a->dtype != LSH_BF16)
+    return fail(LSH_ERR_INVALID, "%s: unknown dtype %d", fn, a->dtype);
+  if (a->reserved != 0) return fail(LSH_ERR_INVALID, "%s: reserved field must be 0", fn);
+  if (a->B < 1 || a->Sq < 1 || a->Skv < 1 || a->H < 1 || a->D < 1)
+    return fail(LSH_ERR_INVALID, "%s: B, Sq, Skv, H, D must be >= 1", fn);
+  if (a->D != LSH_HEAD_DIM)
+    return fail(LSH_ERR_UNSUPPORTED, "%s: head_dim %lld is not supported (only %d)", fn,
+                (long long)a->D, LSH_HEAD_DIM);
+  if (a->dtype != LSH_BF16)
+    return fail(LSH_ERR_UNSUPPORTED, "%s: only bf16 inputs are supported", fn);
+  const int64_t lim = (int64_t)1 << 30;
+  if (a->B >= lim || a->Sq >= lim || a->Skv >= lim || a->H >= lim)
+    return fail(LSH_ERR_UNSUPPORTED, "%s: sizes must be below 2^30", fn);
+  const int64_t big = (int64_t)1 << 31;
+  const int64_t bh = a->B * a->H;
+  if (bh * ((a->Sq + 127) / 128) >= big || bh * ((a->Skv + 127) / 128) >= big ||
+      bh * ((a->Sq + lsh::kBwdQT - 1) / lsh::kBwdQT) * (lsh::kBwdQT / 16) >= big ||
+      a->B * a->Sq * a->H >= big || a->B * a->Skv * a->H >= big)
+    return fail(LSH_ERR_UNSUPPORTED, "%s: B*S*H too large", fn);
+  const void* ptrs[9] = {a->q, a->k, a->v, a->dout, a->o, a->lse, a->dq, a->dk, a->dv};
+  static const char* names[9] = {"q", "k", "v", "dout", "o", "lse", "dq", "dk", "dv"};
+  for (int i = 0; i < 9; ++i) {
+    if (!ptrs[i]) return fail(LSH_ERR_INVALID, "%s: %s is NULL", fn, names[i]);
+    if (!aligned16(ptrs[i]))
+      return fail(LSH_ERR_INVALID, "%s: %s is not 16-byte aligned", fn, names[i]);
+  }
+  if (!std::isfinite(a->scale)) return fail(LSH_ERR_INVALID, "%s: scale must be finite", fn);
+  const int64_t* strides[8] = {a->q_stride, a->k_stride, a->v_stride, a->do_stride,
+                               a->o_stride, a->dq_stride, a->dk_stride, a->dv_stride};
+  const int ebs[8] = {2, 2, 2, 2, 4, 4, 4, 4};
+  for (int t = 0; t < 8; ++t)
+    for (int i = 0; i < 3; ++i) {
+      const int64_t st = strides[t][i];
+      if (st < 0) return fail(LSH_ERR_INVALID, "%s: negative stride", fn);
+      if ((st * ebs[t]) % 16 != 0)
+        return fail(LSH_ERR_INVALID, "%s: stride %lld x %d bytes is not a multiple of 16", fn,
+                    (long long)st, ebs[t]);
+    }
+  // Q, dO, K and V rows are read through buffer descriptors with 32-bit
+  // byte offsets: one head's rows of each must span less than 2 GiB.
+  const int64_t rows[4] = {a->Sq, a->Skv, a->Skv, a->Sq};
+  for (int t = 0; t < 4; ++t)
+    if ((rows[t] - 1) * strides[t][1] * 2 + a->D * 2 >= big)
+      return fail(LSH_ERR_UNSUPPORTED, "%s: the rows of one head span 2 GiB or more", fn);
+  return LSH_OK;
+}
+
+lsh::BwdParams make_bwd_params(const lsh_attn_bwd_args* a, void* workspace) {
+  lsh::BwdParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.dout = a->dout;
+  p.o = a->o;
+  p.lse = a->lse;
+  p.dq = a->dq;
+  p.dk = a->dk;
+  p.dv = a->dv;
+  p.aux = static_cast<float*>(workspace);
+  const int64_t* src[8] = {a->q_stride, a->k_stride, a->v_stride, a->do_stride,
+                           a->o_stride, a->dq_stride, a->dk_stride, a->dv_stride};
+  int64_t* dst[8][3] = {{&p.q_sb, &p.q_ss, &p.q_sh},    {&p.k_sb, &p.k_ss, &p.k_sh},
+                        {&p.v_sb, &p.v_ss, &p.v_sh},    {&p.do_sb, &p.do_ss, &p.do_sh},
+                        {&p.o_sb, &p.o_ss, &p.o_sh},    {&p.dq_sb, &p.dq_ss, &p.dq_sh},
+                        {&p.dk_sb, &p.dk_ss, &p.dk_sh}, {&p.dv_sb, &p.dv_ss, &p.dv_sh}};
+  for (int t = 0; t < 8; ++t)
+    for (int i = 0; i < 3; ++i) *dst[t][i] = src[t][i];
+  p.lse_sb = a->H * a->Sq;
+  p.lse_sh = a->Sq;
+  p.B = (int32_t)a->B;
+  p.H = (int32_t)a->H;
+  p.Sq = (int32_t)a->Sq;
+  p.Skv = (int32_t)a->Skv;
+  p.scale = a->scale;
+  p.scale_log2 = (float)((double)a->scale * 1.4426950408889634);  // scale * log2(e)
+  p.n_qt = (int32_t)((a->Sq + lsh::kBwdQT - 1) / lsh::kBwdQT);
   return p;
 }
 
@@ -374,6 +457,27 @@ lsh_status lsh_attn_fwd_blocksparse(const lsh_attn_args* args, const uint8_t* bl
   if (e != hipSuccess) return hip_status(e, fn);
   p.order = order;
   return hip_status(lsh::launch_attn_sparse(p, static_cast<lsh::DType>(args->dtype), s), fn);
+}
+
+size_t lsh_attn_bwd_workspace(const lsh_attn_bwd_args* args) {
+  if (validate_bwd(args, "lsh_attn_bwd_workspace") != LSH_OK) return 0;
+  const int64_t n_qt = (args->Sq + lsh::kBwdQT - 1) / lsh::kBwdQT;
+  return (size_t)(args->B * args->H * n_qt) * (size_t)(2 * lsh::kBwdQT * sizeof(float));
+}
+
+lsh_status lsh_attn_bwd(const lsh_attn_bwd_args* args, void* workspace, size_t workspace_bytes,
+                        lsh_stream stream) {
+  const char* fn = "lsh_attn_bwd";
+  lsh_status st = validate_bwd(args, fn);
+  if (st != LSH_OK) return st;
+  const size_t need = lsh_attn_bwd_workspace(args);
+  if (!workspace || workspace_bytes < need)
+    return fail(LSH_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(LSH_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+  if ((st = device_check_impl()) != LSH_OK) return st;
+  const lsh::BwdParams p = make_bwd_params(args, workspace);
+  return hip_status(lsh::launch_attn_bwd(p, static_cast<hipStream_t>(stream)), fn);
 }
 
 }  // extern "C"

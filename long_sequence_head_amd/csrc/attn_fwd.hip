@@ -37,7 +37,7 @@
 // work of its neighbour); it serves dense and block-sparse attention. fp32
 // inputs use v_mfma_f32_32x32x2_f32 with the same structure and P kept in
 // fp32.
-#include "lsh_internal.hpp"
+#include "attn_common.hpp"
 
 #include <cstring>
 #include <type_traits>
@@ -45,66 +45,9 @@
 namespace lsh {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-#define LDS_AS __attribute__((address_space(3)))
-
-constexpr float kNegInf = -__builtin_inff();
 // Lazy-rescale threshold in log2 units: the running max is replaced only
 // when a new score exceeds it by more than this.
 constexpr float kRescaleLog2 = 8.0f;
-
-// 16-byte chunk swizzles inside a 256-byte (128 x bf16) LDS row.
-__device__ __forceinline__ int swz_k(int row, int c) { return c ^ (row & 15); }
-__device__ __forceinline__ int swz_v(int row, int c) {
-  return c ^ (((row & 3) << 2) | ((row >> 2) & 3));
-}
-
-// Workgroups are handed to the 8 XCDs round-robin; remap so that each XCD
-// walks a contiguous range of (b, h, query-block) items and the K/V stream
-// of a head is shared inside one XCD's L2.
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
-  constexpr int X = 8;
-  const int per = n / X, rem = n % X;
-  const int x = bid % X, k = bid / X;
-  return x < rem ? x * (per + 1) + k : rem * (per + 1) + (x - rem) * per + k;
-}
-
-// Value of lane l^32 (the other half of the wavefront) for both halves:
-// r[0] + r[1] / max(r[0], r[1]) combine the two halves.
-__device__ __forceinline__ float pair_max(float x) {
-  unsigned u = __builtin_bit_cast(unsigned, x);
-  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  unsigned u = __builtin_bit_cast(unsigned, x);
-  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
-}
-
-__device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0; }
-
-// Item -> (b, h, query block) and the per-item key-tile list.
-struct Item {
-  int b, h, qblk;
-};
-
-__device__ __forceinline__ Item decode_item(int item, int n_qblk, int H) {
-  Item it;
-  it.qblk = item % n_qblk;
-  const int bh = item / n_qblk;
-  it.h = bh % H;
-  it.b = bh / H;
-  return it;
-}
 
 // Builds, in LDS, the ascending list of kept key blocks of one mask row.
 // Returns the number of kept blocks (same value in every thread).
@@ -144,52 +87,6 @@ __device__ __forceinline__ int tile_key0(int t, const unsigned short* kept) {
   } else {
     return t * kBN;
   }
-}
-
-// ------------------------------------------------------- shared helpers
-
-constexpr int kTileBytes = kBN * kD * 2;   // one 64 x 128 bf16 tile
-
-// s_waitcnt with vmcnt = N (6 bits: [3:0] and [15:14]); expcnt and lgkmcnt
-// left at their maximum.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt out of range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-
-__device__ __forceinline__ void barrier_no_fence() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Buffer descriptor over [base, base + rec) bytes, stride 0: loads past rec
-// return zeros.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, int rec) {
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  i32x4 r;
-  r[0] = (int)(uint32_t)a;
-  r[1] = (int)((uint32_t)(a >> 32) & 0xFFFFu);
-  r[2] = rec;
-  r[3] = 0x00020000;
-  return r;
-}
-
-// LDS byte address of a shared-memory pointer.
-__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
-  return (uint32_t)(uintptr_t)(LDS_AS const unsigned char*)p;
-}
-
-// One 1-KiB load of a wavefront into LDS: lane l's 16 bytes at voffset land
-// at LDS address lds + 16 l. Issued from inline asm so that the compiler does
-// not track it: tracked, every control-flow join makes the compiler wait for
-// all such loads in flight before the next LDS read. The kernels order their
-// LDS reads after the data with an explicit s_waitcnt and a barrier.
-__device__ __forceinline__ void lds_dma16(uint32_t lds, uint32_t voffset, const i32x4& rsrc) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(m0v), "v"(voffset), "s"(rsrc) : "memory");
 }
 
 // ------------------------------------ bf16, one wavefront per SIMD, pipelined
@@ -310,35 +207,18 @@ __global__ __launch_bounds__(kSpWaves * 64, 1) void attn_fwd_bf16_sp_kernel(Attn
   };
 
   // ---- LDS fragment offsets inside a tile (per lane, loop-invariant). K
-  // fragment i = 2 s + kb reads row kb*32 + l32, head_dim 16 s + 8 hh .. +7.
-  // V^T fragment i = (kb*2 + jj)*4 + db comes from two transposing reads:
-  // lane (16 g + 4 e + a) points at key kb*32 + jj*16 + 8 part + 4 (g/2) + e,
-  // columns 32 db + 16 (g%2) + 4 a, and receives 4 keys of column 32 db + l%32.
+  // fragment i = 2 s + kb reads row kb*32 + l32, head_dim 16 s + 8 hh .. +7;
+  // V^T fragment i = (kb*2 + jj)*4 + db is a transposing read (tr_read).
   uint32_t kofs[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) kofs[s] = (uint32_t)(l32 * 256 + (swz_k(l32, 2 * s + hh) << 4));
-  const int tg = lane >> 4, te = (lane >> 2) & 3, ta = lane & 3;
   uint32_t vofs[2][4];
-#pragma unroll
-  for (int part = 0; part < 2; ++part)
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int row = 8 * part + 4 * (tg >> 1) + te;
-      const int col = db * 32 + 16 * (tg & 1) + 4 * ta;
-      vofs[part][db] = (uint32_t)(row * 256 + (swz_v(row, col >> 3) << 4) + (col & 7) * 2);
-    }
+  tr_offsets(lane, vofs);
   auto kread = [&](int slot, int i) __device__ -> bf16x8 {
     const LDS_AS unsigned char* b = (LDS_AS const unsigned char*)kslot(slot);
     return *(LDS_AS const bf16x8*)(b + kofs[i >> 1] + (i & 1) * 8192);
   };
-  auto vread = [&](int slot, int i) __device__ -> bf16x8 {
-    const int db = i & 3, jj = (i >> 2) & 1, kb = i >> 3;
-    const LDS_AS unsigned char* b = (LDS_AS const unsigned char*)vslot(slot) + (kb * 32 + jj * 16) * 256;
-    const s16x4 w0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(b + vofs[0][db]));
-    const s16x4 w1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(b + vofs[1][db]));
-    const s16x8 w8 = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8, w8);
-  };
+  auto vread = [&](int slot, int i) __device__ -> bf16x8 { return tr_read(vslot(slot), vofs, i); };
 
   // ---- softmax state
   const float c = p.scale_log2;

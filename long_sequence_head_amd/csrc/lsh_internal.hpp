@@ -53,4 +53,42 @@ hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, int32_
 hipError_t launch_sparse_schedule(const uint8_t* mask, int32_t n_items, int32_t n_mkb,
                                   int32_t* counts, int32_t* order, hipStream_t s);
 
+// Query rows per tile of the backward's per-row workspace (and of the
+// dK/dV kernel's query loop).
+constexpr int kBwdQT = 64;
+
+// Kernel-side description of one attention backward (bf16 Q, K, V, dO;
+// float32 O, LSE and gradients). Strides are in elements.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* o;
+  const float* lse;
+  float* dq;
+  float* dk;
+  float* dv;
+  // Per query row, tile by tile: aux[(b*H + h)*n_qt + t][0..63] = LSE *
+  // log2(e) of rows 64 t .. 64 t + 63 (+inf past Sq), [64..127] =
+  // rowsum(dO * O) of the same rows (0 past Sq).
+  float* aux;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t do_sb, do_ss, do_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int64_t dq_sb, dq_ss, dq_sh;
+  int64_t dk_sb, dk_ss, dk_sh;
+  int64_t dv_sb, dv_ss, dv_sh;
+  int64_t lse_sb, lse_sh;
+  int32_t B, H, Sq, Skv;
+  float scale;        // score multiplier
+  float scale_log2;   // scale * log2(e)
+  int32_t n_qt;       // ceil(Sq / kBwdQT)
+};
+
+// Enqueues the three backward kernels (row statistics, dK/dV, dQ).
+hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t s);
+
 }  // namespace lsh

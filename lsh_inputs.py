@@ -28,7 +28,7 @@ import numpy as np
 ROOT_SEED = 0x15A7_2026
 
 # Stream ids inside one workload's seed sequence.
-_STREAM_Q, _STREAM_K, _STREAM_V, _STREAM_MASK = 0, 1, 2, 3
+_STREAM_Q, _STREAM_K, _STREAM_V, _STREAM_MASK, _STREAM_DO = 0, 1, 2, 3, 4
 
 MASK_BLOCK = 128  # block edge of the block-sparse mask, in tokens
 
@@ -54,7 +54,8 @@ class Workload:
         return 1.0 / math.sqrt(self.D)
 
 
-# The five workloads measured and checked by this repository.
+# The workloads measured and checked by this repository (1-5: forward;
+# 6: the backward of the dense forward at the chunked workload's shape).
 WORKLOADS = {
     1: Workload(1, "dense_f32_B4_S128_H32_D128", "f32", 4, 128, 128, 32, 128),
     2: Workload(2, "ring_partials_bf16_Sq4096_Skv32768_H8_D128", "bf16",
@@ -65,6 +66,7 @@ WORKLOADS = {
                 1, 56160, 56160, 40, 128),
     5: Workload(5, "blocksparse_bf16_S32768_H40_D128_mask128", "bf16",
                 1, 32768, 32768, 40, 128, sparse=True),
+    6: Workload(6, "attn_bwd_bf16_S32760_H40_D128", "bf16", 1, 32760, 32760, 40, 128),
 }
 
 
@@ -129,6 +131,18 @@ def make_qkv(w: Workload, seed: int = 0, Sq: int | None = None, Skv: int | None 
     k = make_tensor((w.B, Skv, w.H, w.D), w.dtype, w.wid, _STREAM_K, seed)
     v = make_tensor((w.B, Skv, w.H, w.D), w.dtype, w.wid, _STREAM_V, seed)
     return q, k, v
+
+
+def make_dout(w: Workload, seed: int = 0, Sq: int | None = None) -> Tensor:
+    """Upstream gradient dO [B, Sq, H, D] of workload ``w`` (iid N(0, 1),
+    rounded to the workload's dtype), from its own seed stream."""
+    Sq = w.Sq if Sq is None else Sq
+    return make_tensor((w.B, Sq, w.H, w.D), w.dtype, w.wid, _STREAM_DO, seed)
+
+
+def make_custom_dout(shape_q, dtype: str, seed: int, wid: int = 99) -> Tensor:
+    """dO for the arbitrary-shape cases of make_custom."""
+    return make_tensor(shape_q, dtype, wid, _STREAM_DO, seed)
 
 
 def make_custom(shape_q, shape_kv, dtype: str, seed: int, wid: int = 99):

@@ -3,6 +3,13 @@ outputs, error measures. Tolerances of the HIP path against the fp64
 oracle (max |difference| over all elements; any NaN or Inf fails):
   O: <= 1e-4 for float32 inputs, <= 2e-2 for bfloat16 inputs (N(0,1) data)
   LSE: <= 1e-3
+Gradients of the backward (bfloat16 inputs; dQ, dK, dV in float32), per
+tensor: max |got - ref| <= 2e-2 * max |ref|. The inputs and dO are exact in
+both; the GPU rounds P and dS to bfloat16 before the products dV = P^T dO,
+dK = scale dS^T Q and dQ = scale dS K (relative error <= 2^-8 per term,
+random in sign, so a sum is off by about 2^-8 / sqrt(3) of its typical
+size), and takes Delta = rowsum(dO * O) from the forward's O, itself within
+the bfloat16 bar above. Measured errors sit near 5e-3 of max |ref|.
 """
 from __future__ import annotations
 
@@ -12,6 +19,7 @@ import numpy as np
 
 TOL_O = {"f32": 1e-4, "bf16": 2e-2}
 TOL_LSE = 1e-3
+TOL_GRAD = 2e-2
 
 
 def torch():
@@ -72,3 +80,19 @@ def check(name, dtype, o_got, lse_got, o_ref, lse_ref, tol_o=None, tol_lse=TOL_L
 
 def announce(msg):
     print(f"[case] {msg}", file=sys.stderr, flush=True)
+
+
+def check_grads(name, got, ref, tol=TOL_GRAD):
+    """got, ref: (dQ, dK, dV) arrays of equal shapes. Each gradient's max
+    abs error must be <= tol * its max |ref|. Returns the relative errors."""
+    errs = []
+    for label, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        r = np.asarray(r, dtype=np.float64)
+        top = float(np.abs(r).max()) if r.size else 0.0
+        e = max_err(g, r)
+        rel = e / top if top > 0 else e
+        errs.append(rel)
+        print(f"[parity] {name} {label}: max|err|={e:.3e} max|ref|={top:.3e} rel={rel:.3e}",
+              file=sys.stderr, flush=True)
+        assert rel <= tol, f"{name}: {label} error {e} > {tol} * {top}"
+    return errs

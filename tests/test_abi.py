@@ -197,3 +197,66 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="build the HIP library"):
         _lib.load(str(tmp_path / "missing.so"))
+
+
+def _valid_bwd_args(B=1, Sq=300, Skv=257, H=4, D=128):
+    a = _lib.AttnBwdArgs()
+    fake = 1 << 20  # 16-byte aligned, never dereferenced
+    (a.q, a.k, a.v, a.dout, a.o, a.lse, a.dq, a.dk, a.dv) = [fake * i for i in range(1, 10)]
+    a.dtype, a.reserved = _lib.LSH_BF16, 0
+    a.B, a.Sq, a.Skv, a.H, a.D = B, Sq, Skv, H, D
+    for f in ("q_stride", "do_stride", "o_stride", "dq_stride"):
+        getattr(a, f)[:] = [Sq * H * D, H * D, D]
+    for f in ("k_stride", "v_stride", "dk_stride", "dv_stride"):
+        getattr(a, f)[:] = [Skv * H * D, H * D, D]
+    a.scale = 0.088
+    return a
+
+
+BWD_BAD_CASES = [
+    ("null dout", lambda a: setattr(a, "dout", None), _lib.LSH_ERR_INVALID),
+    ("null dq", lambda a: setattr(a, "dq", None), _lib.LSH_ERR_INVALID),
+    ("null lse", lambda a: setattr(a, "lse", None), _lib.LSH_ERR_INVALID),
+    ("f32 inputs", lambda a: setattr(a, "dtype", _lib.LSH_F32), _lib.LSH_ERR_UNSUPPORTED),
+    ("bad dtype", lambda a: setattr(a, "dtype", 5), _lib.LSH_ERR_INVALID),
+    ("reserved", lambda a: setattr(a, "reserved", 2), _lib.LSH_ERR_INVALID),
+    ("Skv=0", lambda a: setattr(a, "Skv", 0), _lib.LSH_ERR_INVALID),
+    ("D=64", lambda a: setattr(a, "D", 64), _lib.LSH_ERR_UNSUPPORTED),
+    ("misaligned dk", lambda a: setattr(a, "dk", (1 << 20) + 4), _lib.LSH_ERR_INVALID),
+    ("odd dO stride", lambda a: a.do_stride.__setitem__(1, 4 * 128 + 4), _lib.LSH_ERR_INVALID),
+    ("odd dv stride", lambda a: a.dv_stride.__setitem__(1, 4 * 128 + 2), _lib.LSH_ERR_INVALID),
+    ("inf scale", lambda a: setattr(a, "scale", float("inf")), _lib.LSH_ERR_INVALID),
+    ("huge Skv", lambda a: setattr(a, "Skv", 1 << 30), _lib.LSH_ERR_UNSUPPORTED),
+    # 2^20 query rows x a 2048-element stride x 2 bytes = 4 GiB of one head's rows
+    ("Q span over 2 GiB", lambda a: (setattr(a, "Sq", 1 << 20), a.q_stride.__setitem__(1, 2048)),
+     _lib.LSH_ERR_UNSUPPORTED),
+    ("dO span over 2 GiB", lambda a: (setattr(a, "Sq", 1 << 20), a.do_stride.__setitem__(1, 2048)),
+     _lib.LSH_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("name,mutate,want", BWD_BAD_CASES, ids=[c[0] for c in BWD_BAD_CASES])
+def test_attn_bwd_rejects(name, mutate, want):
+    lib = _lib_or_skip()
+    a = _valid_bwd_args()
+    need = lib.lsh_attn_bwd_workspace(ctypes.byref(a))
+    mutate(a)
+    assert lib.lsh_attn_bwd(ctypes.byref(a), 1 << 24, need, None) == want
+    assert lib.lsh_last_error()
+    assert lib.lsh_attn_bwd_workspace(ctypes.byref(a)) == 0
+
+
+def test_attn_bwd_workspace():
+    lib = _lib_or_skip()
+    a = _valid_bwd_args(B=2, Sq=300, Skv=257, H=4)
+    need = lib.lsh_attn_bwd_workspace(ctypes.byref(a))
+    assert need == 2 * 4 * 5 * 512
+    import torch
+    q = torch.empty(2, 300, 4, 128)
+    assert L.bwd_workspace_bytes(q, None, None) == need
+    assert lib.lsh_attn_bwd(None, 1 << 24, need, None) == _lib.LSH_ERR_INVALID
+    assert lib.lsh_attn_bwd(ctypes.byref(a), 1 << 24, need - 1, None) == _lib.LSH_ERR_WORKSPACE
+    assert lib.lsh_attn_bwd(ctypes.byref(a), None, need, None) == _lib.LSH_ERR_WORKSPACE
+    assert lib.lsh_attn_bwd(ctypes.byref(a), (1 << 24) + 16, need, None) == _lib.LSH_ERR_WORKSPACE
+    if not _torch_cuda():
+        assert lib.lsh_attn_bwd(ctypes.byref(a), 1 << 24, need, None) == _lib.LSH_ERR_NO_DEVICE

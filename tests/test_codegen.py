@@ -16,7 +16,7 @@ import pytest
 
 from long_sequence_head_amd import build as B
 
-SRC = os.path.join(B.CSRC, "attn_fwd.hip")
+SOURCES = ["attn_fwd.hip", "attn_bwd.hip"]
 
 
 def _hipcc():
@@ -26,14 +26,16 @@ def _hipcc():
         return None
 
 
-@pytest.fixture(scope="module")
-def asm(tmp_path_factory):
+@pytest.fixture(scope="module", params=SOURCES)
+def asm(request, tmp_path_factory):
     cc = _hipcc()
     if cc is None:
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("asm") / "attn_fwd.s"
+    src = request.param
+    out = tmp_path_factory.mktemp("asm") / (src + ".s")
     cmd = [cc] + [f for f in B.common_flags() if f not in ("-fPIC",)] + \
-        B.FILE_FLAGS.get("attn_fwd.hip", []) + ["-S", "--cuda-device-only", SRC, "-o", str(out)]
+        B.FILE_FLAGS.get(src, []) + ["-S", "--cuda-device-only", os.path.join(B.CSRC, src),
+                                     "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     return out.read_text()
@@ -51,7 +53,7 @@ def _code_lines(body):
 
 def test_m0_only_feeds_lds_loads(asm):
     funcs = _functions(asm)
-    assert any("attn_fwd_bf16" in n for n in funcs)
+    assert any("attn_fwd_bf16" in n or "attn_bwd_dkdv" in n for n in funcs)
     for name, body in funcs.items():
         lines = _code_lines(body)
         for i, l in enumerate(lines):
@@ -63,7 +65,7 @@ def test_m0_only_feeds_lds_loads(asm):
 
 
 def test_attention_kernels_do_not_spill(asm):
-    sizes = dict(re.findall(r"\.set (_ZN3lsh\S*attn_fwd\S*)\.private_seg_size, (\d+)", asm))
+    sizes = dict(re.findall(r"\.set (_ZN3lsh\S*attn_(?:fwd|bwd)\S*)\.private_seg_size, (\d+)", asm))
     assert sizes, "no attention kernels found"
     for name, size in sizes.items():
         assert int(size) == 0, (name, size)

@@ -133,3 +133,31 @@ def test_workload5_blocksparse(L):
     heads = sorted({int(np.argmin(dens)), int(np.argmax(dens)), 0, 19, 39})
     rows = I.sample_rows(w.Sq, 48, seed=5)
     _check_rows(w.name, w, o, lse, q, k, v, rows, heads, mask=mask)
+
+
+def test_workload6_backward_sampled(L):
+    """Backward at S=32760, H=40 as bench.py runs it (library forward, then
+    lsh_attn_bwd): dQ on sampled query rows and dK, dV on sampled keys of
+    head 37 against the oracle (which still sums over every row and key);
+    the last ragged 128-row block and key block are always included."""
+    w = I.WORKLOADS[6]
+    G.announce(w.name)
+    t = G.torch()
+    (q, k, v), (qg, kg, vg) = _upload(w)
+    do = I.make_dout(w)
+    dog = G.to_gpu(do, w.dtype)
+    o, lse = L.attn_fwd(qg, kg, vg)
+    ws = t.empty(L.bwd_workspace_bytes(qg, kg, vg) + 256, dtype=t.uint8, device="cuda")
+    dq, dk, dv = L.attn_bwd(qg, kg, vg, dog, o, lse, workspace=ws)
+    del o, lse, qg, kg, vg, dog
+    h = 37
+    rows = I.sample_rows(w.Sq, 64, seed=6)
+    keys = I.sample_rows(w.Skv, 64, seed=7)
+    ref = oracle.attention_bwd_ref(q.values, k.values, v.values, do.values, w.scale, rows=rows,
+                                   keys=keys, heads=[h])
+    ridx, kidx = t.from_numpy(rows).cuda(), t.from_numpy(keys).cuda()
+    got = (dq.index_select(1, ridx)[:, :, h].cpu().numpy(),
+           dk.index_select(1, kidx)[:, :, h].cpu().numpy(),
+           dv.index_select(1, kidx)[:, :, h].cpu().numpy())
+    G.check_grads(w.name + " head 37", got, [r[:, :, h] for r in ref])
+    assert t.isfinite(dq).all() and t.isfinite(dk).all() and t.isfinite(dv).all()
