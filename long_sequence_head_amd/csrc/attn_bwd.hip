@@ -24,24 +24,17 @@
 // the definition, in exchange for determinism without atomics and without a
 // quadratic dS buffer.
 //
-// Both streaming kernels run one wavefront per SIMD and keep three LDS slots
-// per streamed tensor: step t issues the loads of tile t + 2 into the slot
-// tile t - 1 left, computes tile t, then waits for tile t + 1 and meets the
-// other wavefronts at one barrier. Each load has two steps to land.
-#include "attn_common.hpp"
+// Both streaming kernels run one wavefront per SIMD, keep three LDS slots
+// per streamed tensor and meet at one barrier per 64-row tile; the work of
+// a wavefront is software-pipelined over 32-row units (see the dK/dV
+// kernel). The dQ kernel lives in attn_bwd_dq.hip: it is compiled with its
+// MFMA results in VGPRs, while dK/dV keeps its 128 accumulators in AGPRs.
+#include "attn_bwd_common.hpp"
 
 namespace lsh {
 namespace {
 
-constexpr int kBwdWaves = 4;
-constexpr int kBwdBlk = kBwdWaves * 32;      // keys (dK/dV) or queries (dQ) per workgroup
-constexpr int kAuxRow = 2 * kBwdQT;          // floats of one aux tile
-constexpr int kAuxBytes = kAuxRow * 4;
 constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ f32x16 mfma16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 // ------------------------------------------------------------- row statistics
 // 16 lanes per query row: lane sub multiplies head_dim 8 sub .. 8 sub + 7,
@@ -75,6 +68,19 @@ __global__ __launch_bounds__(256) void attn_bwd_rows_kernel(BwdParams p) {
 }
 
 // --------------------------------------------------------------------- dK, dV
+// Work of one wavefront is cut into units of 32 queries (two per 64-row
+// tile). Unit u has three parts: A(u), the 16 MFMAs of S and dP; V(u), the
+// vector work that turns them into P and dS (bf16, packed for the next
+// products); B(u), the 16 MFMAs of dV^T += dO^T P and dK^T += Q^T dS. The
+// key loop runs A(u+1) interleaved with V(u), then B(u): the vector work
+// of one unit hides under the matrix work of the next. Fragments are read
+// from LDS two MFMAs ahead of their use.
+//
+// Step t covers units 2t and 2t+1 of tile t: A(2t+1) | V(2t), B(2t), then
+// (once tile t+1 has landed and every wavefront has passed the barrier)
+// A(2t+2) | V(2t+1), B(2t+1). After that barrier no wavefront reads tile
+// t-1 again, so the loads of tile t+2 go into its slot; each tile has about
+// one step to land.
 __global__ __launch_bounds__(kBwdWaves * 64, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   constexpr int LPW = (kTileBytes / 1024) / kBwdWaves;   // 1-KiB loads per wavefront per tensor
   constexpr int LOADS = 2 * LPW + 1;                     // + one for the aux tile
@@ -156,6 +162,14 @@ __global__ __launch_bounds__(kBwdWaves * 64, 1) void attn_bwd_dkdv_kernel(BwdPar
   for (int s = 0; s < 8; ++s) rofs[s] = (uint32_t)(l32 * 256 + (swz_v(l32, 2 * s + hh) << 4));
   uint32_t tofs[2][4];
   tr_offsets(lane, tofs);
+  auto rowread = [&](const unsigned char* tile, int qb, int i) __device__ -> bf16x8 {
+    return *(LDS_AS const bf16x8*)((LDS_AS const unsigned char*)tile + qb * 8192 + rofs[i]);
+  };
+  // LSE * log2(e) (lse = true) or Delta of queries 32 qb + 8 g + 4 hh .. +3
+  auto auxread = [&](const unsigned char* a, bool lse, int qb, int g) __device__ -> f32x4 {
+    const int off = (lse ? 0 : kBwdQT * 4) + (32 * qb + 8 * g + 4 * hh) * 4;
+    return *(LDS_AS const f32x4*)((LDS_AS const unsigned char*)a + off);
+  };
 
   const float c = p.scale_log2;
   f32x16 acc_dv[4], acc_dk[4];   // dV^T, dK^T: [head_dim][key], key = lane
@@ -164,63 +178,96 @@ __global__ __launch_bounds__(kBwdWaves * 64, 1) void attn_bwd_dkdv_kernel(BwdPar
     acc_dv[db] = f32x16{};
     acc_dk[db] = f32x16{};
   }
+  f32x16 sS, sD;            // S and dP of the unit in flight:
+                            // register r <-> query 32 qb + 8 (r / 4) + 4 hh + r % 4
+  bf16x8 pp[2][2], pds[2][2];   // P and dS of two consecutive units, as B operands
 
-  auto compute = [&](int s) __device__ {
-    const unsigned char* tq = qslot(s);
-    const unsigned char* td = dslot(s);
-    const LDS_AS unsigned char* lq = (LDS_AS const unsigned char*)tq;
-    const LDS_AS unsigned char* ld = (LDS_AS const unsigned char*)td;
-    const LDS_AS unsigned char* la = (LDS_AS const unsigned char*)aslot(s);
+  // A(unit qa of tiles tq/td): S and dP into sS, sD
+  auto phase_a = [&](const unsigned char* tq, const unsigned char* td, int qa) __device__ {
+    bf16x8 fq[8], fd[8];
+    fq[0] = rowread(tq, qa, 0);
+    fd[0] = rowread(td, qa, 0);
+    fq[1] = rowread(tq, qa, 1);
+    fd[1] = rowread(td, qa, 1);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      // S and dP of queries 32 qb + 8 (r / 4) + 4 hh + r % 4 (register r)
-      // and this lane's key
-      f32x16 sc = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bf16x8 aq = *(LDS_AS const bf16x8*)(lq + qb * 8192 + rofs[i]);
-        const bf16x8 ad = *(LDS_AS const bf16x8*)(ld + qb * 8192 + rofs[i]);
-        sc = mfma16(aq, kf[i], sc);
-        dp = mfma16(ad, vf[i], dp);
+    for (int i = 0; i < 16; ++i) {
+      const int k = i >> 1;
+      if ((i & 1) == 0) {
+        if (k + 2 < 8) fq[k + 2] = rowread(tq, qa, k + 2);
+        sS = mfma16(fq[k], kf[k], k == 0 ? f32x16{} : sS);
+      } else {
+        if (k + 2 < 8) fd[k + 2] = rowread(td, qa, k + 2);
+        sD = mfma16(fd[k], vf[k], k == 0 ? f32x16{} : sD);
       }
-      // P = exp2(S c - LSE log2 e), dS = P (dP - Delta), packed in the order
-      // tr_read expects
-      bf16x8 pp[2], pds[2];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // B(unit qb of tiles tq/td, P and dS from set sb): dV^T += dO^T P,
+  // dK^T += Q^T dS, interleaved (if DO_V) with V of the unit in sS/sD
+  // (block qv of aux tile ta) into set sv.
+  auto phase_bv = [&](const bool DO_B, const unsigned char* tq, const unsigned char* td, int qb,
+                      int sb, const bool DO_V, const unsigned char* ta, int qv, int sv) __device__ {
+    auto frag = [&](int m) __device__ -> bf16x8 {
+      const int i = (qb * 2 + (m >> 3)) * 4 + ((m >> 1) & 3);
+      return tr_read((m & 1) ? tq : td, tofs, i);
+    };
+    bf16x8 f[16];
+    f32x4 l4[4], d4[4];
+    if (DO_B) {
+      f[0] = frag(0);
+      f[1] = frag(1);
+    }
+    if (DO_V) {
+      l4[0] = auxread(ta, true, qv, 0);
+      d4[0] = auxread(ta, false, qv, 0);
+    }
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int row = 32 * qb + 8 * g + 4 * hh;
-        const f32x4 l4 = *(LDS_AS const f32x4*)(la + row * 4);
-        const f32x4 d4 = *(LDS_AS const f32x4*)(la + kBwdQT * 4 + row * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c, -l4[e]));
-          const float ds = pr * (dp[r] - d4[e]);
-          pp[r >> 3][r & 7] = (__bf16)pr;
-          pds[r >> 3][r & 7] = (__bf16)ds;
-        }
+    for (int m = 0; m < 16; ++m) {
+      if (DO_B) {
+        if (m + 2 < 16) f[m + 2] = frag(m + 2);
+        const int jj = m >> 3, db = (m >> 1) & 3;
+        if (m & 1)
+          acc_dk[db] = mfma16(f[m], pds[sb][jj], acc_dk[db]);
+        else
+          acc_dv[db] = mfma16(f[m], pp[sb][jj], acc_dv[db]);
       }
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int i = (qb * 2 + jj) * 4 + db;
-          acc_dv[db] = mfma16(tr_read(td, tofs, i), pp[jj], acc_dv[db]);
-          acc_dk[db] = mfma16(tr_read(tq, tofs, i), pds[jj], acc_dk[db]);
+      if (DO_V) {
+        const int r = m, g = r >> 2, e = r & 3;
+        if (e == 0 && g + 1 < 4) {
+          l4[g + 1] = auxread(ta, true, qv, g + 1);
+          d4[g + 1] = auxread(ta, false, qv, g + 1);
         }
+        const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sS[r], c, -l4[g][e]));
+        asm volatile("" ::"v"(x));   // computed here, next to this MFMA
+        const float y = x * (sD[r] - d4[g][e]);
+        pp[sv][r >> 3][r & 7] = (__bf16)x;
+        pds[sv][r >> 3][r & 7] = (__bf16)y;
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   const int n_t = p.n_qt;
-  auto step = [&](int s, int t) __device__ {
-    if (t + 2 < n_t) issue(t + 2, (s + 2) % 3);
-    compute(s);
-    if (t + 1 < n_t) {
-      if (t + 2 < n_t) wait_vmcnt<LOADS>();
-      else wait_vmcnt<0>();
+  // step t: units 2t (P, dS in set 0) and 2t+1 (set 1) of tile t
+  auto step = [&](int s, int t, const bool HAS_NEXT) __device__ {
+    const unsigned char* tq = qslot(s);
+    const unsigned char* td = dslot(s);
+    const unsigned char* ta = aslot(s);
+    const int s1 = (s + 1) % 3;
+    phase_a(tq, td, 1);
+    phase_bv(true, tq, td, 0, 0, true, ta, 1, 1);
+    if (HAS_NEXT) {
+      wait_vmcnt<0>();   // tile t+1 (the only loads in flight)
       barrier_no_fence();
+      if (t + 2 < n_t) issue(t + 2, (s + 2) % 3);
+      phase_a(qslot(s1), dslot(s1), 0);
+      phase_bv(true, tq, td, 1, 1, true, aslot(s1), 0, 0);
+    } else {
+      phase_bv(true, tq, td, 1, 1, false, ta, 0, 0);
     }
   };
+
   issue(0, 0);
   if (n_t > 1) {
     issue(1, 1);
@@ -229,14 +276,27 @@ __global__ __launch_bounds__(kBwdWaves * 64, 1) void attn_bwd_dkdv_kernel(BwdPar
     wait_vmcnt<0>();
   }
   barrier_no_fence();
+  phase_a(lq0, ld0, 0);
+  phase_bv(false, lq0, ld0, 0, 0, true, la0, 0, 0);
+  // t is a multiple of 3 at the top of the loop, so every slot index is a
+  // compile-time constant.
   int t = 0;
-  for (; t + 3 <= n_t; t += 3) {
-    step(0, t);
-    step(1, t + 1);
-    step(2, t + 2);
+  for (; t + 3 < n_t; t += 3) {
+    step(0, t, true);
+    step(1, t + 1, true);
+    step(2, t + 2, true);
   }
-  if (t < n_t) step(0, t);
-  if (t + 1 < n_t) step(1, t + 1);
+  const int rest = n_t - t;   // 1, 2 or 3
+  if (rest == 3) {
+    step(0, t, true);
+    step(1, t + 1, true);
+    step(2, t + 2, false);
+  } else if (rest == 2) {
+    step(0, t, true);
+    step(1, t + 1, false);
+  } else {
+    step(0, t, false);
+  }
 
   // ---- epilogue: lane = key, registers = head_dim 32 db + 8 g4 + 4 hh + 0..3
   if (!k_ok) return;
@@ -258,164 +318,6 @@ __global__ __launch_bounds__(kBwdWaves * 64, 1) void attn_bwd_dkdv_kernel(BwdPar
     }
 }
 
-// ------------------------------------------------------------------------- dQ
-__global__ __launch_bounds__(kBwdWaves * 64, 1) void attn_bwd_dq_kernel(BwdParams p) {
-  constexpr int LPW = (kTileBytes / 1024) / kBwdWaves;
-  constexpr int LOADS = 2 * LPW;
-  static_assert(LPW * kBwdWaves * 1024 == kTileBytes, "tile/threads mismatch");
-
-  __shared__ __attribute__((aligned(1024))) unsigned char lk0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char lk1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char lk2[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char lv0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char lv1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char lv2[kTileBytes];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hh = lane >> 5;
-
-  const int n_qblk = (p.Sq + kBwdBlk - 1) / kBwdBlk;
-  const int item = xcd_remap(blockIdx.x, gridDim.x);
-  const int qblk = item % n_qblk, bh = item / n_qblk;
-  const int h = bh % p.H, b = bh / p.H;
-  const int qi = qblk * kBwdBlk + wave * 32 + l32;
-  const bool q_ok = qi < p.Sq;
-  const __bf16* qp = static_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh;
-  const __bf16* kp = static_cast<const __bf16*>(p.k) + b * p.k_sb + h * p.k_sh;
-  const __bf16* vp = static_cast<const __bf16*>(p.v) + b * p.v_sb + h * p.v_sh;
-  const __bf16* dop = static_cast<const __bf16*>(p.dout) + b * p.do_sb + h * p.do_sh;
-
-  // Q and dO of this lane's query: the B operands of S^T = K Q^T and
-  // dP^T = V dO^T. Rows past Sq get LSE = +inf, so their P is 0.
-  bf16x8 qf[8], df[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    qf[s] = q_ok ? *reinterpret_cast<const bf16x8*>(qp + (int64_t)qi * p.q_ss + 16 * s + 8 * hh)
-                 : bf16x8{};
-    df[s] = q_ok ? *reinterpret_cast<const bf16x8*>(dop + (int64_t)qi * p.do_ss + 16 * s + 8 * hh)
-                 : bf16x8{};
-  }
-  float lse2 = __builtin_inff(), delta = 0.0f;
-  if (q_ok) {
-    const float* a = p.aux + ((int64_t)bh * p.n_qt + qi / kBwdQT) * kAuxRow + (qi % kBwdQT);
-    lse2 = a[0];
-    delta = a[kBwdQT];
-  }
-
-  const uint32_t k_rb = (uint32_t)(p.k_ss * 2), v_rb = (uint32_t)(p.v_ss * 2);
-  const int k_rec = (int)((uint32_t)(p.Skv - 1) * k_rb + kD * 2);
-  const int v_rec = (int)((uint32_t)(p.Skv - 1) * v_rb + kD * 2);
-  uint32_t koff[LPW], voff[LPW];
-#pragma unroll
-  for (int j = 0; j < LPW; ++j) {
-    const int r = 4 * (wave * LPW + j) + (lane >> 4);
-    const uint32_t c16 = (uint32_t)swz_v(r, lane & 15) << 4;
-    koff[j] = (uint32_t)r * k_rb + c16;
-    voff[j] = (uint32_t)r * v_rb + c16;
-  }
-  const i32x4 k_rsrc = make_rsrc(kp, k_rec), v_rsrc = make_rsrc(vp, v_rec);
-  auto kslot = [&](int s) __device__ -> unsigned char* { return s == 0 ? lk0 : s == 1 ? lk1 : lk2; };
-  auto vslot = [&](int s) __device__ -> unsigned char* { return s == 0 ? lv0 : s == 1 ? lv1 : lv2; };
-  auto issue = [&](int t, int s) __device__ {
-    const uint32_t bk = (uint32_t)t * kBN * k_rb, bv = (uint32_t)t * kBN * v_rb;
-    const uint32_t dst_k = lds_addr(kslot(s)) + wave * LPW * 1024;
-    const uint32_t dst_v = lds_addr(vslot(s)) + wave * LPW * 1024;
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) lds_dma16(dst_k + j * 1024, koff[j] + bk, k_rsrc);
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) lds_dma16(dst_v + j * 1024, voff[j] + bv, v_rsrc);
-  };
-
-  uint32_t rofs[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) rofs[s] = (uint32_t)(l32 * 256 + (swz_v(l32, 2 * s + hh) << 4));
-  uint32_t tofs[2][4];
-  tr_offsets(lane, tofs);
-
-  const float c = p.scale_log2;
-  f32x16 acc[4];   // dQ^T: [head_dim][query], query = lane
-#pragma unroll
-  for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
-
-  auto compute = [&](int s, int t) __device__ {
-    const unsigned char* tk = kslot(s);
-    const LDS_AS unsigned char* lk = (LDS_AS const unsigned char*)tk;
-    const LDS_AS unsigned char* lv = (LDS_AS const unsigned char*)vslot(s);
-    const int lim = p.Skv - t * kBN - 4 * hh;   // keys at tile offset >= lim + 4 hh are past Skv
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // S^T and dP^T of keys 32 kb + 8 (r / 4) + 4 hh + r % 4 (register r)
-      // and this lane's query
-      f32x16 st = f32x16{}, dpt = f32x16{};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bf16x8 ak = *(LDS_AS const bf16x8*)(lk + kb * 8192 + rofs[i]);
-        const bf16x8 av = *(LDS_AS const bf16x8*)(lv + kb * 8192 + rofs[i]);
-        st = mfma16(ak, qf[i], st);
-        dpt = mfma16(av, df[i], dpt);
-      }
-      if (t * kBN + kBN > p.Skv) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * kb + 8 * (r >> 2) + (r & 3) >= lim) st[r] = kNegInf;
-      }
-      bf16x8 pds[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], c, -lse2));
-        pds[r >> 3][r & 7] = (__bf16)(pr * (dpt[r] - delta));
-      }
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-          acc[db] = mfma16(tr_read(tk, tofs, (kb * 2 + jj) * 4 + db), pds[jj], acc[db]);
-    }
-  };
-
-  const int n_t = (p.Skv + kBN - 1) / kBN;
-  auto step = [&](int s, int t) __device__ {
-    if (t + 2 < n_t) issue(t + 2, (s + 2) % 3);
-    compute(s, t);
-    if (t + 1 < n_t) {
-      if (t + 2 < n_t) wait_vmcnt<LOADS>();
-      else wait_vmcnt<0>();
-      barrier_no_fence();
-    }
-  };
-  issue(0, 0);
-  if (n_t > 1) {
-    issue(1, 1);
-    wait_vmcnt<LOADS>();
-  } else {
-    wait_vmcnt<0>();
-  }
-  barrier_no_fence();
-  int t = 0;
-  for (; t + 3 <= n_t; t += 3) {
-    step(0, t);
-    step(1, t + 1);
-    step(2, t + 2);
-  }
-  if (t < n_t) step(0, t);
-  if (t + 1 < n_t) step(1, t + 1);
-
-  // ---- epilogue: lane = query, registers = head_dim 32 db + 8 g4 + 4 hh + 0..3
-  if (!q_ok) return;
-  float* dqp = p.dq + b * p.dq_sb + h * p.dq_sh + (int64_t)qi * p.dq_ss;
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = db * 32 + 8 * g4 + 4 * hh;
-      f32x4 q4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) q4[i] = acc[db][4 * g4 + i] * p.scale;
-      *reinterpret_cast<f32x4*>(dqp + d) = q4;
-    }
-}
-
 }  // namespace
 
 hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t s) {
@@ -429,10 +331,7 @@ hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t s) {
                      s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t n_qblk = (p.Sq + kBwdBlk - 1) / kBwdBlk;
-  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)(bh * n_qblk)), dim3(kBwdWaves * 64), 0, s,
-                     p);
-  return hipGetLastError();
+  return launch_attn_bwd_dq(p, s);
 }
 
 }  // namespace lsh

@@ -90,5 +90,7 @@ struct BwdParams {
 
 // Enqueues the three backward kernels (row statistics, dK/dV, dQ).
 hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t s);
+// Enqueues the dQ kernel alone (the last of the three).
+hipError_t launch_attn_bwd_dq(const BwdParams& p, hipStream_t s);
 
 }  // namespace lsh

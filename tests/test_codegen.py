@@ -16,7 +16,7 @@ import pytest
 
 from long_sequence_head_amd import build as B
 
-SOURCES = ["attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip"]
 
 
 def _hipcc():
@@ -53,7 +53,7 @@ def _code_lines(body):
 
 def test_m0_only_feeds_lds_loads(asm):
     funcs = _functions(asm)
-    assert any("attn_fwd_bf16" in n or "attn_bwd_dkdv" in n for n in funcs)
+    assert any(k in n for n in funcs for k in ("attn_fwd_bf16", "attn_bwd_dkdv", "attn_bwd_dq"))
     for name, body in funcs.items():
         lines = _code_lines(body)
         for i, l in enumerate(lines):
