@@ -9,7 +9,8 @@ both; the GPU rounds P and dS to bfloat16 before the products dV = P^T dO,
 dK = scale dS^T Q and dQ = scale dS K (relative error <= 2^-8 per term,
 random in sign, so a sum is off by about 2^-8 / sqrt(3) of its typical
 size), and takes Delta = rowsum(dO * O) from the forward's O, itself within
-the bfloat16 bar above. Measured errors sit near 5e-3 of max |ref|.
+the bfloat16 bar above. Measured over the backward cases: median 2.0e-3,
+largest 4.5e-3 of max |ref| (peaked scores).
 """
 from __future__ import annotations
 
