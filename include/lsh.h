@@ -196,9 +196,18 @@ lsh_status lsh_head_permute(const void* src, void* dst, int32_t dtype,
  * excluded from the softmax. A query row with no kept block gets O = 0 and
  * LSE = -inf. Requires a bf16 or f32 args as lsh_attn_fwd, Skv >= 1.
  * workspace: at least lsh_attn_fwd_blocksparse_workspace(args) bytes; it
- * holds the per-(b, h, query-block) kept-block counts and the work order
- * (query blocks sorted by decreasing kept count, so the heaviest start
- * first). Same reuse rule as the chunked workspace.
+ * holds the launch schedule, readable after the call for diagnostics. With
+ * n = B * H * ceil(Sq/128) items (item = (b * H + h) * ceil(Sq/128) + query
+ * block) and R = n * 4 rounded up to 256 bytes:
+ *   int32 counts[n]     at byte 0:     kept blocks of each item's mask row;
+ *   int32 order[n]      at byte R:     item of each launch slot;
+ *   int64 totals[B * H] at byte 2 * R: kept blocks of each head.
+ * Heads go in descending total (ties: lower index first) and, inside a
+ * head, items in descending count (ties: lower index first). Launch slots
+ * are handed to the 8 XCDs in turn, so each XCD works through one head's
+ * rows at a time (sharing its K/V in L2), every XCD gets an equal share of
+ * each head, and the heaviest rows of a head start first. Same reuse rule
+ * as the chunked workspace.
  */
 lsh_status lsh_attn_fwd_blocksparse(const lsh_attn_args* args,
                                     const uint8_t* block_mask,

@@ -426,7 +426,8 @@ lsh_status lsh_head_permute(const void* src, void* dst, int32_t dtype, int64_t B
 size_t lsh_attn_fwd_blocksparse_workspace(const lsh_attn_args* args) {
   if (validate_attn(args, false, "lsh_attn_fwd_blocksparse_workspace") != LSH_OK) return 0;
   const int64_t n_items = args->B * args->H * ((args->Sq + LSH_MASK_BLOCK - 1) / LSH_MASK_BLOCK);
-  return 2 * round_up((size_t)n_items * sizeof(int32_t), 256);
+  return 2 * round_up((size_t)n_items * sizeof(int32_t), 256) +
+         round_up((size_t)(args->B * args->H) * sizeof(long long), 256);
 }
 
 lsh_status lsh_attn_fwd_blocksparse(const lsh_attn_args* args, const uint8_t* block_mask,
@@ -449,11 +450,14 @@ lsh_status lsh_attn_fwd_blocksparse(const lsh_attn_args* args, const uint8_t* bl
   p.n_mqb = (int32_t)n_mqb;
   p.n_mkb = (int32_t)n_mkb;
   const int32_t n_items = (int32_t)(args->B * args->H * n_mqb);
+  // workspace: int32 counts[n_items] | int32 order[n_items] | int64 totals[B * H]
+  const size_t region = round_up((size_t)n_items * sizeof(int32_t), 256);
   int32_t* counts = static_cast<int32_t*>(workspace);
-  int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
-                                              round_up((size_t)n_items * sizeof(int32_t), 256));
+  int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + region);
+  long long* totals = reinterpret_cast<long long*>(static_cast<char*>(workspace) + 2 * region);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = lsh::launch_sparse_schedule(block_mask, n_items, p.n_mkb, counts, order, s);
+  hipError_t e = lsh::launch_sparse_schedule(block_mask, n_items, p.n_mkb, p.n_mqb, counts, totals,
+                                             order, s);
   if (e != hipSuccess) return hip_status(e, fn);
   p.order = order;
   return hip_status(lsh::launch_attn_sparse(p, static_cast<lsh::DType>(args->dtype), s), fn);

@@ -138,41 +138,69 @@ __global__ __launch_bounds__(256) void sparse_count_kernel(const uint8_t* __rest
   if (lane == 0) counts[item] = cnt;
 }
 
-// order[rank(i)] = i with rank(i) = #{j : c_j > c_i} + #{j < i : c_j = c_i}
-// (c = counts): descending count, ascending item index among equal counts,
-// so the order is deterministic. A workgroup ranks 64 items; its 16
-// wavefronts split the j range, reading the counts from LDS in chunks
-// (every lane of a wavefront reads the same entry: a broadcast).
-constexpr int kRankWaves = 16;
-constexpr int kRankChunk = 4096;
+// Launch order of the block-sparse work items. Item i = g * per + r is
+// query block r of head g = b * H + h. Heads go in descending total kept
+// count (ties: lower head index first); inside a head, query blocks go in
+// descending kept count (ties: lower index first). Consecutive launch slots
+// go to the 8 XCDs in turn, so each XCD runs rows of one head at a time (its
+// 32 CUs share that head's K/V tiles in their L2) and every XCD gets an
+// equal share of every head; inside a head the heaviest rows start first.
 
-__global__ __launch_bounds__(kRankWaves * 64) void sparse_rank_kernel(const int* __restrict__ counts,
-                                                                     int n,
-                                                                     int* __restrict__ order) {
-  __shared__ int cbuf[kRankChunk];
-  __shared__ int part[kRankWaves][64];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int i = blockIdx.x * 64 + lane;
-  const int c_i = i < n ? counts[i] : 0;
-  int r = 0;
-  for (int base = 0; base < n; base += kRankChunk) {
-    const int m = n - base < kRankChunk ? n - base : kRankChunk;
+// Kept-block total of each head: one wavefront per head (exact integer sum).
+__global__ __launch_bounds__(256) void sparse_total_kernel(const int* __restrict__ counts,
+                                                           int n_groups, int per,
+                                                           long long* __restrict__ totals) {
+  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (g >= n_groups) return;
+  const int* c = counts + (int64_t)g * per;
+  long long t = 0;
+  for (int j = lane; j < per; j += 64) t += c[j];
+  for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
+  if (lane == 0) totals[g] = t;
+}
+
+// order[per * rank(g) + rank_g(r)] = g * per + r, with
+//   rank(g)   = #{k : T_k > T_g} + #{k < g : T_k = T_g}            (T = totals)
+//   rank_g(r) = #{j : c_j > c_r} + #{j < r : c_j = c_r} over the head's
+//               query blocks (c = counts).
+// A workgroup ranks 256 query blocks of one head, reading the head's counts
+// from LDS in chunks (every lane reads the same entry: a broadcast).
+constexpr int kOrderThreads = 256;
+constexpr int kOrderChunk = 4096;
+
+__global__ __launch_bounds__(kOrderThreads) void sparse_order_kernel(
+    const int* __restrict__ counts, const long long* __restrict__ totals, int n_groups, int per,
+    int* __restrict__ order) {
+  __shared__ int cbuf[kOrderChunk];
+  __shared__ int grank;
+  const int blocks_per_group = (per + kOrderThreads - 1) / kOrderThreads;
+  const int g = blockIdx.x / blocks_per_group;
+  const int r = (blockIdx.x % blocks_per_group) * kOrderThreads + threadIdx.x;
+  if (threadIdx.x == 0) grank = 0;
+  __syncthreads();
+  const long long t_g = totals[g];
+  int gr = 0;
+  for (int k = threadIdx.x; k < n_groups; k += kOrderThreads) {
+    const long long t_k = totals[k];
+    gr += (t_k > t_g) | ((t_k == t_g) & (k < g));
+  }
+  atomicAdd(&grank, gr);   // integer: the sum is exact in any order
+  const int* c = counts + (int64_t)g * per;
+  const int c_r = r < per ? c[r] : 0;
+  int lr = 0;
+  for (int base = 0; base < per; base += kOrderChunk) {
+    const int m = per - base < kOrderChunk ? per - base : kOrderChunk;
     __syncthreads();
-    for (int j = threadIdx.x; j < m; j += kRankWaves * 64) cbuf[j] = counts[base + j];
+    for (int j = threadIdx.x; j < m; j += kOrderThreads) cbuf[j] = c[base + j];
     __syncthreads();
-    for (int jj = w; jj < m; jj += kRankWaves) {
-      const int c_j = cbuf[jj];
-      r += (c_j > c_i) | ((c_j == c_i) & (base + jj < i));
+    for (int j = 0; j < m; ++j) {
+      const int c_j = cbuf[j];
+      lr += (c_j > c_r) | ((c_j == c_r) & (base + j < r));
     }
   }
-  part[w][lane] = r;
   __syncthreads();
-  if (w == 0 && i < n) {
-    int rank = 0;
-#pragma unroll
-    for (int k = 0; k < kRankWaves; ++k) rank += part[k][lane];
-    order[rank] = i;
-  }
+  if (r < per) order[(int64_t)grank * per + lr] = g * per + r;
 }
 
 }  // namespace
@@ -200,14 +228,21 @@ hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, int32_
   return hipGetLastError();
 }
 
-hipError_t launch_sparse_schedule(const uint8_t* mask, int32_t n_items, int32_t n_mkb,
-                                  int32_t* counts, int32_t* order, hipStream_t s) {
+hipError_t launch_sparse_schedule(const uint8_t* mask, int32_t n_items, int32_t n_mkb, int32_t per,
+                                  int32_t* counts, long long* totals, int32_t* order,
+                                  hipStream_t s) {
   hipLaunchKernelGGL(sparse_count_kernel, dim3((n_items + 3) / 4), dim3(256), 0, s, mask, n_items,
                      n_mkb, counts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(sparse_rank_kernel, dim3((n_items + 63) / 64), dim3(kRankWaves * 64), 0, s, counts,
-                     n_items, order);
+  const int n_groups = n_items / per;
+  hipLaunchKernelGGL(sparse_total_kernel, dim3((n_groups + 3) / 4), dim3(256), 0, s, counts,
+                     n_groups, per, totals);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int blocks_per_group = (per + kOrderThreads - 1) / kOrderThreads;
+  hipLaunchKernelGGL(sparse_order_kernel, dim3((unsigned)((int64_t)n_groups * blocks_per_group)),
+                     dim3(kOrderThreads), 0, s, counts, totals, n_groups, per, order);
   return hipGetLastError();
 }
 

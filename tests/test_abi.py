@@ -185,7 +185,7 @@ def test_blocksparse_validation():
     lib = _lib_or_skip()
     a = _valid_args(Sq=300, Skv=257, H=4)
     need = lib.lsh_attn_fwd_blocksparse_workspace(ctypes.byref(a))
-    assert need == 2 * ((4 * 3 * 4 + 255) // 256 * 256)
+    assert need == 2 * ((4 * 3 * 4 + 255) // 256 * 256) + (4 * 8 + 255) // 256 * 256
     m = 1 << 22
     assert lib.lsh_attn_fwd_blocksparse(ctypes.byref(a), None, m, need, None) == _lib.LSH_ERR_INVALID
     assert lib.lsh_attn_fwd_blocksparse(ctypes.byref(a), m, m, need - 1, None) == _lib.LSH_ERR_WORKSPACE

@@ -306,6 +306,54 @@ def test_blocksparse_diagonal_is_blockwise_dense(L):
         assert t.equal(o1[:, sl], o2) and t.equal(l1[:, :, sl], l2), i
 
 
+def _expected_schedule(mask):
+    """The launch schedule lsh.h documents, computed from the mask."""
+    B, H, nq, _ = mask.shape
+    counts = (mask != 0).sum(axis=-1).reshape(-1).astype(np.int64)
+    totals = counts.reshape(B * H, nq).sum(axis=1)
+    heads = sorted(range(B * H), key=lambda g: (-totals[g], g))
+    order = []
+    for g in heads:
+        order += [g * nq + r for r in sorted(range(nq), key=lambda r: (-counts[g * nq + r], r))]
+    return counts, totals, np.array(order, dtype=np.int64)
+
+
+def _read_schedule(ws, n, n_heads):
+    region = (n * 4 + 255) // 256 * 256
+    raw = ws.cpu().numpy()
+    counts = raw[:n * 4].view(np.int32)
+    order = raw[region:region + n * 4].view(np.int32)
+    totals = raw[2 * region:2 * region + n_heads * 8].view(np.int64)
+    return counts, totals, order
+
+
+@pytest.mark.parametrize("case", [(2, 700, 900, 3, 0), (1, 4097 * 128, 128, 1, 1)],
+                         ids=["B2_H3", "4097_query_blocks"])
+def test_blocksparse_schedule(L, case):
+    """The schedule left in the workspace equals its definition (exact
+    integer comparison). Equal masks across batch entries tie the head
+    totals; the second case has more query blocks per head than one LDS
+    chunk of the ranking kernel, with counts of 0 or 1 only."""
+    B, Sq, Skv, H, seed = case
+    G.announce(f"sparse schedule B={B} Sq={Sq} Skv={Skv} H={H}")
+    t = G.torch()
+    nq, nk = -(-Sq // 128), -(-Skv // 128)
+    mask, _ = I.make_block_mask(B, H, nq, nk, seed=seed, lo=0.2, hi=0.8)
+    if nk == 1:   # one key block: drop the diagonal rule so that rows differ
+        mask = I.rng_for(5, 3, seed + 100).integers(0, 2, size=mask.shape).astype(np.uint8)
+    q, k, v = I.make_custom((B, Sq, H, 128), (B, Skv, H, 128), "bf16", seed=17)
+    qg, kg, vg = G.to_gpu(q, "bf16"), G.to_gpu(k, "bf16"), G.to_gpu(v, "bf16")
+    need = L.blocksparse_workspace_bytes(qg, kg, vg)
+    ws = t.zeros(need, dtype=t.uint8, device="cuda")
+    assert ws.data_ptr() % 256 == 0
+    L.attn_fwd_blocksparse(qg, kg, vg, t.from_numpy(mask).cuda(), workspace=ws)
+    t.cuda.synchronize()
+    want = _expected_schedule(mask)
+    got = _read_schedule(ws, B * H * nq, B * H)
+    for name, g, w in zip(("counts", "totals", "order"), got, want):
+        assert np.array_equal(g.astype(np.int64), w), name
+
+
 @pytest.mark.parametrize("Skv", [1, 63, 64, 65, 128, 129, 191, 333, 1000, 4097])
 def test_large_grid_ragged_keys(L, Skv):
     """A grid of 1032 workgroups (several per CU over time): sampled query
