@@ -175,6 +175,29 @@ def bench_ring(L, I, w, steps, warmup):
     return r
 
 
+def sparse_imbalance(I, w, mask, ws):
+    """Imbalance ratios (max / mean kept blocks per part) of the block-sparse
+    work: under an 8-way head split (contiguous, and sparsity-aware), an
+    8-way query-row split, and the GPU's own launch schedule read back from
+    the workspace of the last timed call (per XCD, and the simulated
+    makespan of the 256 CUs against a perfectly balanced one)."""
+    from long_sequence_head_amd import balance as BL
+    counts = BL.kept_counts(mask)
+    n = counts.size
+    off = (ws.data_ptr() + 255) // 256 * 256 - ws.data_ptr()
+    g_counts, g_order, g_totals = BL.schedule_from_workspace(ws.cpu().numpy(), n, w.B * w.H, off)
+    if g_counts.tolist() != counts.ravel().tolist():
+        raise RuntimeError("block-sparse schedule in the workspace does not match the mask")
+    sched = BL.schedule_loads(g_counts, g_order)
+    _, bal = BL.balanced_head_split(counts, 8)
+    return {"definition": "max / mean kept 128x128 blocks per part",
+            "head_split_contiguous_8": BL.imbalance_ratio(BL.ulysses_head_loads(counts, 8)),
+            "head_split_balanced_8": BL.imbalance_ratio(bal),
+            "row_split_contiguous_8": BL.imbalance_ratio(BL.ring_row_loads(counts, 8)),
+            "gpu_schedule_xcd": sched["xcd_ratio"],
+            "gpu_schedule_cu_makespan": sched["makespan_ratio"]}
+
+
 def bench_sparse(L, I, w, steps, warmup):
     import torch
     log(f"[bench] workload {w.wid}: {w.name}: generating inputs")
@@ -193,9 +216,11 @@ def bench_sparse(L, I, w, steps, warmup):
     flops = nnz * 4 * I.MASK_BLOCK * I.MASK_BLOCK * w.D
     r = dict(ms=ms, tflops=flops / ms / 1e9, kept_blocks=nnz, kept_flops=flops,
              density_mean=float(dens.mean()), density_min=float(dens.min()),
-             density_max=float(dens.max()))
+             density_max=float(dens.max()),
+             imbalance=sparse_imbalance(I, w, mask, ws))
     log(f"[bench] workload {w.wid}: {ms:.3f} ms, {r['tflops']:.1f} TFLOP/s on kept blocks "
-        f"(mean density {r['density_mean']:.3f})")
+        f"(mean density {r['density_mean']:.3f}); imbalance " +
+        ", ".join(f"{k} {v:.3f}" for k, v in r["imbalance"].items() if k != "definition"))
     return r
 
 

@@ -16,6 +16,10 @@ Functions:
   head_permute        [B, S, H, D] -> [B, hc, S, D] copy of heads [h0, h0+hc)
   attn_fwd_blocksparse  attention restricted to a 128x128 block mask
   attn_bwd            gradients dQ, dK, dV of the dense forward (bf16)
+
+Submodule balance: host-side load-balance diagnostics of the block-sparse
+work (imbalance ratios of head and row splits, and of the launch schedule
+the library leaves in its workspace).
 """
 from __future__ import annotations
 
