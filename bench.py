@@ -294,7 +294,19 @@ def cpu_baseline(I, w, q, k, v, o_gpu, lse_gpu, target_s):
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"query rows 0..{n - 1} of head 0 against all {w.Skv} keys "
                       f"({flops / 1e9:.1f} GFLOP, fp64 numpy, {t:.1f} s)",
+            "blas": blas_name(),
             "gpu_vs_oracle_on_sample": {"max_abs_dO": err_o, "max_abs_dLSE": err_l}}
+
+
+def blas_name():
+    """BLAS library numpy calls (name and version from threadpoolctl)."""
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info()
+                if i.get("user_api") == "blas"]
+        return ", ".join(libs) or "unknown"
+    except Exception:   # pragma: no cover
+        return "unknown"
 
 
 def traffic_entry(achieved_launch_ms):

@@ -3,6 +3,12 @@ outputs, error measures. Tolerances of the HIP path against the fp64
 oracle (max |difference| over all elements; any NaN or Inf fails):
   O: <= 1e-4 for float32 inputs, <= 2e-2 for bfloat16 inputs (N(0,1) data)
   LSE: <= 1e-3
+For bfloat16 inputs the 2e-2 bar is the worst case of rounding every
+attention weight to bfloat16, so it alone would miss, e.g., a dropped key
+tile at long S. Checks that pass `sigma` (bf16_weight_sigma: the per-element
+standard deviation of that rounding error, from the oracle) also fail when
+an O error exceeds SIGMA_ALARM = 8 sigma (+1e-6); the largest seen over
+every bf16 case is 3.5 sigma.
 Gradients of the backward (bfloat16 inputs; dQ, dK, dV in float32), per
 tensor: max |got - ref| <= 2e-2 * max |ref|. The inputs and dO are exact in
 both; the GPU rounds P and dS to bfloat16 before the products dV = P^T dO,
@@ -21,6 +27,8 @@ import numpy as np
 TOL_O = {"f32": 1e-4, "bf16": 2e-2}
 TOL_LSE = 1e-3
 TOL_GRAD = 2e-2
+U_BF16 = 2.0 ** -8   # unit roundoff of bfloat16 (round to nearest even)
+SIGMA_ALARM = 8.0    # bf16 O errors beyond this many sigma of weight rounding fail
 
 
 def torch():
@@ -69,13 +77,41 @@ def max_err(got, want) -> float:
     return float(d.max()) if d.size else 0.0
 
 
-def check(name, dtype, o_got, lse_got, o_ref, lse_ref, tol_o=None, tol_lse=TOL_LSE):
+def bf16_weight_sigma(oracle, q, k, v, scale, lse_ref, **kw):
+    """Per-element standard deviation of the O error that rounding each
+    attention weight to bfloat16 causes, from the oracle alone.
+
+    With weights w_j = softmax_j(s) and relative rounding errors d_j of
+    zero mean and variance <= U_BF16^2 / 3 (round to nearest even), the error
+    sum_j w_j d_j v_j has variance <= U_BF16^2 / 3 * sum_j w_j^2 v_j^2, and
+      sum_j w_j^2 v_j^2 = exp(LSE(2 s) - 2 LSE(s)) * sum_j softmax_j(2 s) v_j^2,
+    i.e. one more oracle call with scale doubled and V squared. Rows with no
+    key (LSE = -inf) get 0. kw is passed through (rows, heads, block_mask)."""
+    v2 = np.square(np.asarray(v, dtype=np.float32))   # exact: bf16 values square into 16 bits
+    o2, lse2 = oracle.attention_ref(q, k, v2, 2.0 * scale, **kw)
+    with np.errstate(invalid="ignore", over="ignore"):
+        ratio = np.where(np.isfinite(lse_ref), np.exp(lse2 - 2.0 * lse_ref), 0.0)
+    ratio = np.nan_to_num(ratio)                              # [B, H, rows]
+    var = np.transpose(ratio, (0, 2, 1))[..., None] * np.nan_to_num(o2)
+    return U_BF16 / np.sqrt(3.0) * np.sqrt(np.maximum(var, 0.0))
+
+
+def check(name, dtype, o_got, lse_got, o_ref, lse_ref, tol_o=None, tol_lse=TOL_LSE, sigma=None):
     eo = max_err(o_got, o_ref)
     el = max_err(lse_got, lse_ref)
-    print(f"[parity] {name}: max|dO|={eo:.3e} max|dLSE|={el:.3e}", file=sys.stderr, flush=True)
+    ratio, rmax = "", None
+    if sigma is not None:
+        with np.errstate(invalid="ignore"):
+            r = np.abs(np.asarray(o_got, np.float64) - np.asarray(o_ref, np.float64)) / (sigma + 1e-6)
+        rmax = float(np.nanmax(r)) if np.isfinite(eo) else float("inf")
+        ratio = f" max|dO|/(sigma+1e-6)={rmax:.2f}"
+    print(f"[parity] {name}: max|dO|={eo:.3e} max|dLSE|={el:.3e}{ratio}", file=sys.stderr, flush=True)
     tol_o = TOL_O[dtype] if tol_o is None else tol_o
     assert eo <= tol_o, f"{name}: O error {eo} > {tol_o}"
     assert el <= tol_lse, f"{name}: LSE error {el} > {tol_lse}"
+    if rmax is not None:
+        assert rmax <= SIGMA_ALARM, (f"{name}: O error {rmax:.2f} sigma of bf16 weight rounding "
+                                     f"(alarm at {SIGMA_ALARM})")
     return eo, el
 
 

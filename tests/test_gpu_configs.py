@@ -34,7 +34,12 @@ def _check_rows(name, w, o, lse, q, k, v, rows, heads, mask=None):
     og = o.index_select(1, ridx).cpu().numpy()
     lg = lse.index_select(2, ridx).cpu().numpy()
     hs = list(heads)
-    return G.check(name, w.dtype, og[:, :, hs], lg[:, hs], o_ref[:, :, hs], lse_ref[:, hs])
+    sig = None
+    if w.dtype == "bf16":
+        sig = G.bf16_weight_sigma(oracle, q.values, k.values, v.values, w.scale, lse_ref, rows=rows,
+                                  heads=heads, block_mask=mask)[:, :, hs]
+    return G.check(name, w.dtype, og[:, :, hs], lg[:, hs], o_ref[:, :, hs], lse_ref[:, hs],
+                   sigma=sig)
 
 
 def test_workload1_dense_f32_full(L):

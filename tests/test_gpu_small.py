@@ -37,7 +37,10 @@ def test_dense_vs_oracle(L, dtype, shape):
     o, lse = G.poisoned_outputs(B, Sq, H)
     L.attn_fwd(G.to_gpu(q, dtype), G.to_gpu(k, dtype), G.to_gpu(v, dtype), o=o, lse=lse)
     o_ref, lse_ref = oracle.attention_ref(q.values, k.values, v.values, 1 / math.sqrt(128))
-    G.check(f"dense {dtype} {shape}", dtype, o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+    sig = (G.bf16_weight_sigma(oracle, q.values, k.values, v.values, 1 / math.sqrt(128), lse_ref)
+           if dtype == "bf16" else None)
+    G.check(f"dense {dtype} {shape}", dtype, o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref,
+            sigma=sig)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -92,7 +95,9 @@ def test_strided_packed_qkv(L, dtype):
     lse = t.full((B, H, S), float("nan"), dtype=t.float32, device="cuda")
     L.attn_fwd(qv, kv, vv, o=o, lse=lse)
     o_ref, lse_ref = oracle.attention_ref(q.values, k.values, v.values, 1 / math.sqrt(D))
-    G.check(f"strided {dtype}", dtype, o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+    sig = (G.bf16_weight_sigma(oracle, q.values, k.values, v.values, 1 / math.sqrt(D), lse_ref)
+           if dtype == "bf16" else None)
+    G.check(f"strided {dtype}", dtype, o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, sigma=sig)
     assert t.isnan(wide[:, :, 0]).all() and t.isnan(wide[:, :, H + 1]).all(), "wrote outside O"
 
 
@@ -106,7 +111,9 @@ def test_peaked_scores(L, dtype):
     o, lse = G.poisoned_outputs(B, Sq, H)
     L.attn_fwd(G.values_to_gpu(qv, dtype), G.to_gpu(k, dtype), G.to_gpu(v, dtype), o=o, lse=lse)
     o_ref, lse_ref = oracle.attention_ref(qv, k.values, v.values, 1 / math.sqrt(D))
-    G.check(f"peaked {dtype}", dtype, o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+    sig = (G.bf16_weight_sigma(oracle, qv, k.values, v.values, 1 / math.sqrt(D), lse_ref)
+           if dtype == "bf16" else None)
+    G.check(f"peaked {dtype}", dtype, o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, sigma=sig)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -131,7 +138,10 @@ def test_monotone_scores(L, dtype, direction):
     o, lse = G.poisoned_outputs(B, Sq, H)
     L.attn_fwd(G.values_to_gpu(q, dtype), G.values_to_gpu(k, dtype), G.to_gpu(v, dtype), o=o, lse=lse)
     o_ref, lse_ref = oracle.attention_ref(q, k, v.values, 1 / math.sqrt(D))
-    G.check(f"monotone {dtype} {direction}", dtype, o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+    sig = (G.bf16_weight_sigma(oracle, q, k, v.values, 1 / math.sqrt(D), lse_ref)
+           if dtype == "bf16" else None)
+    G.check(f"monotone {dtype} {direction}", dtype, o.cpu().numpy(), lse.cpu().numpy(), o_ref,
+            lse_ref, sigma=sig)
 
 
 def test_run_to_run_bit_identical(L):
@@ -277,7 +287,10 @@ def test_blocksparse_vs_oracle(L, dtype, case):
                            t.from_numpy(mask).cuda(), o=o, lse=lse)
     o_ref, lse_ref = oracle.attention_ref(q.values, k.values, v.values, 1 / math.sqrt(128),
                                           block_mask=mask)
-    G.check(f"sparse {dtype} {case}", dtype, o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+    sig = (G.bf16_weight_sigma(oracle, q.values, k.values, v.values, 1 / math.sqrt(128), lse_ref,
+                               block_mask=mask) if dtype == "bf16" else None)
+    G.check(f"sparse {dtype} {case}", dtype, o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref,
+            sigma=sig)
 
 
 def test_blocksparse_all_ones_equals_dense_bitwise(L):
@@ -364,6 +377,8 @@ def test_large_grid_ragged_keys(L, Skv):
     assert not t.isnan(o).any() and not t.isnan(lse).any(), "unwritten output"
     rows = I.sample_rows(Sq, 200, seed=Skv)
     o_ref, lse_ref = oracle.attention_ref(q.values, k.values, v.values, 1 / math.sqrt(128), rows=rows)
+    sig = G.bf16_weight_sigma(oracle, q.values, k.values, v.values, 1 / math.sqrt(128), lse_ref,
+                              rows=rows)
     ridx = t.from_numpy(rows).cuda()
     G.check(f"large grid Skv={Skv}", "bf16", o.index_select(1, ridx).cpu().numpy(),
-            lse.index_select(2, ridx).cpu().numpy(), o_ref, lse_ref)
+            lse.index_select(2, ridx).cpu().numpy(), o_ref, lse_ref, sigma=sig)

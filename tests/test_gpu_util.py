@@ -1,0 +1,38 @@
+"""CPU checks of the parity-test helpers in tests/gpu_util.py."""
+import math
+
+import numpy as np
+
+import oracle
+from tests import gpu_util as G
+
+
+def test_bf16_weight_sigma_equals_direct_sum():
+    """sigma = 2^-8 / sqrt(3) * sqrt(sum_j w_j^2 v_j^2), with the weights
+    w = softmax(scale q k^T) formed directly here, on a tiny case with a
+    block mask that empties one query block."""
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((2, 5, 2, 8))
+    k = rng.standard_normal((2, 7, 2, 8))
+    v = rng.standard_normal((2, 7, 2, 8)).astype(np.float32)
+    sc = 0.3
+    o, lse = oracle.attention_ref(q, k, v, sc)
+    sig = G.bf16_weight_sigma(oracle, q, k, v, sc, lse)
+    s = np.einsum("bihd,bjhd->bhij", q, k) * sc
+    w = np.exp(s - s.max(-1, keepdims=True))
+    w /= w.sum(-1, keepdims=True)
+    direct = G.U_BF16 / math.sqrt(3) * np.sqrt(
+        np.einsum("bhij,bjhd->bihd", w ** 2, v.astype(np.float64) ** 2))
+    assert np.allclose(sig, direct, rtol=1e-6, atol=1e-12)
+
+
+def test_bf16_weight_sigma_empty_rows_are_zero():
+    rng = np.random.default_rng(1)
+    q = rng.standard_normal((1, 200, 1, 4))
+    k = rng.standard_normal((1, 300, 1, 4))
+    v = rng.standard_normal((1, 300, 1, 4)).astype(np.float32)
+    mask = np.ones((1, 1, 2, 3), dtype=np.uint8)
+    mask[0, 0, 1] = 0                       # query rows 128..199 attend to nothing
+    o, lse = oracle.attention_ref(q, k, v, 0.5, block_mask=mask)
+    sig = G.bf16_weight_sigma(oracle, q, k, v, 0.5, lse, block_mask=mask)
+    assert np.all(sig[:, 128:] == 0) and np.all(sig[:, :128] > 0)
