@@ -69,16 +69,18 @@ __global__ __launch_bounds__(256) void attn_bwd_rows_kernel(BwdParams p) {
 
 // --------------------------------------------------------------------- dK, dV
 // Work of one wavefront is cut into units of 32 queries (two per 64-row
-// tile). Unit u has three parts: A(u), the 16 MFMAs of S and dP; V(u), the
-// vector work that turns them into P and dS (bf16, packed for the next
-// products); B(u), the 16 MFMAs of dV^T += dO^T P and dK^T += Q^T dS. The
-// key loop runs A(u+1) interleaved with V(u), then B(u): the vector work
-// of one unit hides under the matrix work of the next. Fragments are read
-// from LDS two MFMAs ahead of their use.
+// tile). Unit u has three parts: A(u), the 16 MFMAs of S and dP; E(u), the
+// elementwise work that turns them into P and dS (bf16, packed as the B
+// operands of the next products); B(u), the 16 MFMAs of dV^T += dO^T P and
+// dK^T += Q^T dS. The loop runs A(u) alone, then B(u-1) interleaved with
+// E(u): the elementwise work of one unit hides under the gradient products
+// of the previous one, and only one unit's S and dP are live at a time
+// (P and dS are double-buffered instead). Fragments are read from LDS two
+// MFMAs ahead of their use.
 //
-// Step t covers units 2t and 2t+1 of tile t: A(2t+1) | V(2t), B(2t), then
+// Step t covers units 2t and 2t+1 of tile t: A(2t+1), B(2t) | E(2t+1), then
 // (once tile t+1 has landed and every wavefront has passed the barrier)
-// A(2t+2) | V(2t+1), B(2t+1). After that barrier no wavefront reads tile
+// A(2t+2), B(2t+1) | E(2t+2). After that barrier no wavefront reads tile
 // t-1 again, so the loads of tile t+2 go into its slot; each tile has about
 // one step to land.
 __global__ __launch_bounds__(kBwdWaves * 64, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
@@ -204,10 +206,10 @@ __global__ __launch_bounds__(kBwdWaves * 64, 1) void attn_bwd_dkdv_kernel(BwdPar
   };
 
   // B(unit qb of tiles tq/td, P and dS from set sb): dV^T += dO^T P,
-  // dK^T += Q^T dS, interleaved (if DO_V) with V of the unit in sS/sD
-  // (block qv of aux tile ta) into set sv.
-  auto phase_bv = [&](const bool DO_B, const unsigned char* tq, const unsigned char* td, int qb,
-                      int sb, const bool DO_V, const unsigned char* ta, int qv, int sv) __device__ {
+  // dK^T += Q^T dS, interleaved (if DO_E) with E of the unit in sS/sD
+  // (block qe of aux tile ta) into set se.
+  auto phase_be = [&](const bool DO_B, const unsigned char* tq, const unsigned char* td, int qb,
+                      int sb, const bool DO_E, const unsigned char* ta, int qe, int se) __device__ {
     auto frag = [&](int m) __device__ -> bf16x8 {
       const int i = (qb * 2 + (m >> 3)) * 4 + ((m >> 1) & 3);
       return tr_read((m & 1) ? tq : td, tofs, i);
@@ -218,9 +220,9 @@ __global__ __launch_bounds__(kBwdWaves * 64, 1) void attn_bwd_dkdv_kernel(BwdPar
       f[0] = frag(0);
       f[1] = frag(1);
     }
-    if (DO_V) {
-      l4[0] = auxread(ta, true, qv, 0);
-      d4[0] = auxread(ta, false, qv, 0);
+    if (DO_E) {
+      l4[0] = auxread(ta, true, qe, 0);
+      d4[0] = auxread(ta, false, qe, 0);
     }
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
@@ -232,17 +234,17 @@ __global__ __launch_bounds__(kBwdWaves * 64, 1) void attn_bwd_dkdv_kernel(BwdPar
         else
           acc_dv[db] = mfma16(f[m], pp[sb][jj], acc_dv[db]);
       }
-      if (DO_V) {
+      if (DO_E) {
         const int r = m, g = r >> 2, e = r & 3;
         if (e == 0 && g + 1 < 4) {
-          l4[g + 1] = auxread(ta, true, qv, g + 1);
-          d4[g + 1] = auxread(ta, false, qv, g + 1);
+          l4[g + 1] = auxread(ta, true, qe, g + 1);
+          d4[g + 1] = auxread(ta, false, qe, g + 1);
         }
         const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sS[r], c, -l4[g][e]));
         asm volatile("" ::"v"(x));   // computed here, next to this MFMA
         const float y = x * (sD[r] - d4[g][e]);
-        pp[sv][r >> 3][r & 7] = (__bf16)x;
-        pds[sv][r >> 3][r & 7] = (__bf16)y;
+        pp[se][r >> 3][r & 7] = (__bf16)x;
+        pds[se][r >> 3][r & 7] = (__bf16)y;
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -256,15 +258,15 @@ __global__ __launch_bounds__(kBwdWaves * 64, 1) void attn_bwd_dkdv_kernel(BwdPar
     const unsigned char* ta = aslot(s);
     const int s1 = (s + 1) % 3;
     phase_a(tq, td, 1);
-    phase_bv(true, tq, td, 0, 0, true, ta, 1, 1);
+    phase_be(true, tq, td, 0, 0, true, ta, 1, 1);
     if (HAS_NEXT) {
       wait_vmcnt<0>();   // tile t+1 (the only loads in flight)
       barrier_no_fence();
       if (t + 2 < n_t) issue(t + 2, (s + 2) % 3);
       phase_a(qslot(s1), dslot(s1), 0);
-      phase_bv(true, tq, td, 1, 1, true, aslot(s1), 0, 0);
+      phase_be(true, tq, td, 1, 1, true, aslot(s1), 0, 0);
     } else {
-      phase_bv(true, tq, td, 1, 1, false, ta, 0, 0);
+      phase_be(true, tq, td, 1, 1, false, ta, 0, 0);
     }
   };
 
@@ -277,7 +279,7 @@ __global__ __launch_bounds__(kBwdWaves * 64, 1) void attn_bwd_dkdv_kernel(BwdPar
   }
   barrier_no_fence();
   phase_a(lq0, ld0, 0);
-  phase_bv(false, lq0, ld0, 0, 0, true, la0, 0, 0);
+  phase_be(false, lq0, ld0, 0, 0, true, la0, 0, 0);
   // t is a multiple of 3 at the top of the loop, so every slot index is a
   // compile-time constant.
   int t = 0;

@@ -6,9 +6,13 @@ namespace lsh {
 namespace {
 
 // ------------------------------------------------------------------------- dQ
-// Same pipeline with units of 32 keys (two per 64-key tile): A(u) is S^T
-// and dP^T (16 MFMAs, queries in lanes), V(u) masks keys past Skv and forms
-// dS^T, B(u) is dQ^T += K^T dS^T (8 MFMAs).
+// Units of 32 keys (two per 64-key tile): A(u) is S^T and dP^T (16 MFMAs,
+// queries in lanes), E(u) masks keys past Skv and forms dS^T (bf16, packed
+// as the B operand of the next product), B(u) is dQ^T += K^T dS^T (8
+// MFMAs). The loop runs A(u+1) interleaved with E(u), then B(u): the
+// elementwise work of one unit hides under the matrix work of the next
+// (both units' S^T and dP^T are live, which the VGPR budget of this pass
+// allows). Tiles, slots and barriers are as in the dK/dV pass.
 __global__ __launch_bounds__(kBwdWaves * 64, 1) void attn_bwd_dq_kernel(BwdParams p) {
   constexpr int LPW = (kTileBytes / 1024) / kBwdWaves;
   constexpr int LOADS = 2 * LPW;
@@ -105,8 +109,8 @@ __global__ __launch_bounds__(kBwdWaves * 64, 1) void attn_bwd_dq_kernel(BwdParam
   };
 
   auto phase_a = [&](const bool DO_A, const unsigned char* tk, const unsigned char* tv, int ka,
-                     const bool DO_V, f32x16& st, f32x16& dpt, const f32x16& sv,
-                     const f32x16& dv) __device__ {
+                     const bool DO_E, f32x16& st, f32x16& dpt, const f32x16& se,
+                     const f32x16& de) __device__ {
     bf16x8 fk[8], fv[8];
     if (DO_A) {
       fk[0] = rowread(tk, ka, 0);
@@ -126,11 +130,11 @@ __global__ __launch_bounds__(kBwdWaves * 64, 1) void attn_bwd_dq_kernel(BwdParam
           dpt = mfma16(fv[k], df[k], k == 0 ? f32x16{} : dpt);
         }
       }
-      if (DO_V) {
+      if (DO_E) {
         const int r = i;
-        const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], c, -lse2));
+        const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(se[r], c, -lse2));
         asm volatile("" ::"v"(x));   // computed here, next to this MFMA
-        pds[r >> 3][r & 7] = (__bf16)(x * (dv[r] - delta));
+        pds[r >> 3][r & 7] = (__bf16)(x * (de[r] - delta));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
