@@ -260,3 +260,22 @@ def test_attn_bwd_workspace():
     assert lib.lsh_attn_bwd(ctypes.byref(a), (1 << 24) + 16, need, None) == _lib.LSH_ERR_WORKSPACE
     if not _torch_cuda():
         assert lib.lsh_attn_bwd(ctypes.byref(a), 1 << 24, need, None) == _lib.LSH_ERR_NO_DEVICE
+
+
+def test_row_span_limit_is_exact():
+    """One head's rows may span up to 2^31 - 1 bytes: with 64 interleaved
+    heads (16 KiB per row) 131072 rows are accepted and 131073 are not, for
+    K/V in the forward and Q/dO in the backward."""
+    lib = _lib_or_skip()
+    ok = _lib.LSH_ERR_NO_DEVICE if not _torch_cuda() else _lib.LSH_OK
+    a = _valid_args(Sq=130, Skv=131072, H=64)
+    assert lib.lsh_attn_fwd(ctypes.byref(a), None) in (ok, _lib.LSH_ERR_NO_DEVICE)
+    a = _valid_args(Sq=130, Skv=131073, H=64)
+    assert lib.lsh_attn_fwd(ctypes.byref(a), None) == _lib.LSH_ERR_UNSUPPORTED
+    b = _valid_bwd_args(Sq=131072, Skv=200, H=64)
+    need = lib.lsh_attn_bwd_workspace(ctypes.byref(b))
+    assert need > 0
+    if not _torch_cuda():
+        assert lib.lsh_attn_bwd(ctypes.byref(b), 1 << 24, need, None) == _lib.LSH_ERR_NO_DEVICE
+    b = _valid_bwd_args(Sq=131073, Skv=200, H=64)
+    assert lib.lsh_attn_bwd(ctypes.byref(b), 1 << 24, 1 << 40, None) == _lib.LSH_ERR_UNSUPPORTED
