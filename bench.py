@@ -178,9 +178,10 @@ def bench_ring(L, I, w, steps, warmup):
 def sparse_imbalance(I, w, mask, ws):
     """Imbalance ratios (max / mean kept blocks per part) of the block-sparse
     work: under an 8-way head split (contiguous, and sparsity-aware), an
-    8-way query-row split, and the GPU's own launch schedule read back from
-    the workspace of the last timed call (per XCD, and the simulated
-    makespan of the 256 CUs against a perfectly balanced one)."""
+    8-way query-row split, the best 8-device grid of head groups x row
+    ranges, and the GPU's own launch schedule read back from the workspace
+    of the last timed call (per XCD, and the simulated makespan of the 256
+    CUs against a perfectly balanced one)."""
     from long_sequence_head_amd import balance as BL
     counts = BL.kept_counts(mask)
     n = counts.size
@@ -190,7 +191,10 @@ def sparse_imbalance(I, w, mask, ws):
         raise RuntimeError("block-sparse schedule in the workspace does not match the mask")
     sched = BL.schedule_loads(g_counts, g_order)
     _, bal = BL.balanced_head_split(counts, 8)
+    best = BL.dual_level_plan(counts, 8)[0]
     return {"definition": "max / mean kept 128x128 blocks per part",
+            "dual_level_best_8": {"head_groups": best["Ph"], "row_ranges": best["Pr"],
+                                  "ratio": best["ratio"]},
             "head_split_contiguous_8": BL.imbalance_ratio(BL.ulysses_head_loads(counts, 8)),
             "head_split_balanced_8": BL.imbalance_ratio(bal),
             "row_split_contiguous_8": BL.imbalance_ratio(BL.ring_row_loads(counts, 8)),
@@ -220,7 +224,8 @@ def bench_sparse(L, I, w, steps, warmup):
              imbalance=sparse_imbalance(I, w, mask, ws))
     log(f"[bench] workload {w.wid}: {ms:.3f} ms, {r['tflops']:.1f} TFLOP/s on kept blocks "
         f"(mean density {r['density_mean']:.3f}); imbalance " +
-        ", ".join(f"{k} {v:.3f}" for k, v in r["imbalance"].items() if k != "definition"))
+        ", ".join(f"{k} {v:.3f}" for k, v in r["imbalance"].items()
+                  if isinstance(v, float)))
     return r
 
 

@@ -24,6 +24,12 @@ Functions:
   balanced_head_split     a sparsity-aware split of the heads: heaviest head
                           first, to the least-loaded part that still has
                           room (every part gets H / P heads)
+  balanced_row_split      the contiguous split of the query rows into P
+                          ranges with the smallest largest load
+  dual_level_plan         P devices as a grid of Ph head groups x Pr row
+                          ranges, every factorization P = Ph * Pr tried
+                          (the page's dual-level partitioning with its
+                          degrees chosen from the mask)
   schedule_from_workspace the launch schedule lsh_attn_fwd_blocksparse
                           leaves in its workspace
   schedule_loads          per-XCD loads of that schedule and the makespan
@@ -37,7 +43,8 @@ import heapq
 import numpy as np
 
 __all__ = ["kept_counts", "imbalance_ratio", "ulysses_head_loads", "ring_row_loads",
-           "balanced_head_split", "schedule_from_workspace", "schedule_loads"]
+           "balanced_head_split", "balanced_row_split", "dual_level_plan",
+           "schedule_from_workspace", "schedule_loads"]
 
 
 def kept_counts(mask) -> np.ndarray:
@@ -102,6 +109,78 @@ def balanced_head_split(counts, parts: int):
     return assign, loads
 
 
+def balanced_row_split(row_loads, parts: int):
+    """Contiguous split of rows (in order) into `parts` non-empty ranges
+    whose largest load is as small as possible: a binary search on that
+    load, each candidate checked by filling ranges greedily. Returns
+    (range boundaries [0 = b_0 < ... < b_parts = n], loads)."""
+    w = np.asarray(row_loads, dtype=np.int64).ravel()
+    n = w.size
+    if parts < 1 or parts > n:
+        raise ValueError(f"cannot split {n} rows into {parts} parts")
+
+    def cuts_for(cap):
+        # greedy: close a range when the next row would exceed cap, keeping
+        # enough rows for the remaining ranges
+        bounds, acc, left = [0], 0, parts
+        for i in range(n):
+            rows_after = n - i
+            if bounds[-1] < i and (acc + w[i] > cap or rows_after < left):
+                bounds.append(i)
+                acc, left = 0, left - 1
+            if w[i] > cap:
+                return None
+            acc += w[i]
+        if len(bounds) > parts:
+            return None
+        # split the largest ranges further until there are `parts` of them
+        while len(bounds) < parts:
+            spans = [(bounds[j + 1] if j + 1 < len(bounds) else n) - bounds[j]
+                     for j in range(len(bounds))]
+            j = max(range(len(spans)), key=lambda q: (spans[q], -q))
+            bounds.insert(j + 1, bounds[j] + spans[j] // 2)
+        return bounds + [n]
+
+    lo, hi = int(w.max(initial=0)), int(w.sum())
+    while lo < hi:
+        mid = (lo + hi) // 2
+        if cuts_for(mid) is None:
+            lo = mid + 1
+        else:
+            hi = mid
+    bounds = cuts_for(lo)
+    loads = np.array([w[bounds[p]:bounds[p + 1]].sum() for p in range(parts)], dtype=np.int64)
+    return bounds, loads
+
+
+def dual_level_plan(counts, devices: int):
+    """Every grid Ph x Pr = devices with H % Ph == 0 and Pr <= query rows:
+    heads split into Ph groups by balanced_head_split, each group's rows
+    (its kept blocks summed over its heads) into Pr ranges by
+    balanced_row_split. Returns the plans sorted by imbalance ratio (then
+    fewer head groups), each a dict with Ph, Pr, the ratio and the device
+    loads."""
+    c = np.asarray(counts, dtype=np.int64)
+    B, H, n_qb = c.shape
+    plans = []
+    for ph in range(1, devices + 1):
+        if devices % ph or H % ph:
+            continue
+        pr = devices // ph
+        if pr > n_qb:
+            continue
+        groups, _ = balanced_head_split(c, ph)
+        loads = []
+        for heads in groups:
+            rows = c[:, heads, :].sum(axis=(0, 1))
+            loads.extend(balanced_row_split(rows, pr)[1].tolist())
+        loads = np.array(loads, dtype=np.int64)
+        plans.append({"Ph": ph, "Pr": pr, "ratio": imbalance_ratio(loads), "loads": loads})
+    if not plans:
+        raise ValueError(f"no grid of {devices} devices fits H={H} and {n_qb} query rows")
+    return sorted(plans, key=lambda d: (d["ratio"], d["Ph"]))
+
+
 def schedule_from_workspace(ws, n_items: int, n_heads: int, offset: int = 0):
     """(counts, order, totals) from the bytes of a block-sparse workspace
     (the layout lsh.h documents: int32 counts[n], int32 order[n], int64
@@ -145,6 +224,7 @@ def schedule_loads(counts, order, n_xcd: int = 8, cus_per_xcd: int = 32,
             heapq.heappush(free, (t + d, cu))
             end = max(end, t + d)
         makespan = max(makespan, end)
-    ideal = dur.sum() / (n_xcd * cus_per_xcd)
+    ideal = float(dur.sum()) / (n_xcd * cus_per_xcd)
     return {"xcd_loads": xcd_loads, "xcd_ratio": imbalance_ratio(xcd_loads),
-            "makespan": makespan, "makespan_ratio": 1.0 if ideal == 0 else makespan / ideal}
+            "makespan": float(makespan),
+            "makespan_ratio": 1.0 if ideal == 0 else float(makespan) / ideal}

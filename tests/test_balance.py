@@ -108,3 +108,41 @@ def test_descending_order_beats_ascending_on_cus():
     a = BL.schedule_loads(counts, asc, n_xcd=1, cus_per_xcd=2)
     d = BL.schedule_loads(counts, desc, n_xcd=1, cus_per_xcd=2)
     assert a["makespan"] == 9 and d["makespan"] == 6
+
+
+def test_balanced_row_split_is_optimal_by_brute_force():
+    import itertools
+    rng = np.random.default_rng(7)
+    for _ in range(120):
+        n = int(rng.integers(1, 9))
+        parts = int(rng.integers(1, n + 1))
+        w = rng.integers(0, 10, size=n)
+        bounds, loads = BL.balanced_row_split(w, parts)
+        assert bounds[0] == 0 and bounds[-1] == n and len(bounds) == parts + 1
+        assert all(bounds[i] < bounds[i + 1] for i in range(parts))
+        assert loads.sum() == w.sum()
+        best = min(max(w[x[i]:x[i + 1]].sum() for i in range(parts))
+                   for cuts in itertools.combinations(range(1, n), parts - 1)
+                   for x in [[0, *cuts, n]])
+        assert loads.max() == best
+
+
+def test_balanced_row_split_hand_case():
+    bounds, loads = BL.balanced_row_split([1, 1, 1, 1, 4], 2)
+    assert loads.max() == 4 and bounds == [0, 4, 5]
+    with pytest.raises(ValueError):
+        BL.balanced_row_split([1, 2], 3)
+
+
+def test_dual_level_plan_picks_the_better_grid():
+    # head 0 keeps 8 blocks in its first row, head 1 one block per row.
+    # 1 x 2 grid: rows 9, 1, 1, 1 -> best cut 9 | 3 -> ratio 9 / 6 = 1.5;
+    # 2 x 1 grid: heads 8 | 4 -> ratio 8 / 6.
+    c = _counts([[8, 0, 0, 0], [1, 1, 1, 1]])
+    plans = BL.dual_level_plan(c, 2)
+    assert [(p["Ph"], p["Pr"]) for p in plans] == [(2, 1), (1, 2)]
+    assert plans[0]["ratio"] == pytest.approx(8 / 6)
+    assert plans[1]["ratio"] == pytest.approx(9 / 6)
+    assert plans[0]["loads"].tolist() == [8, 4]
+    with pytest.raises(ValueError):
+        BL.dual_level_plan(_counts([[1]]), 2)   # one head, one row: no 2-device grid
