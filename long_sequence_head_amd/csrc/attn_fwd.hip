@@ -32,11 +32,15 @@
 //    in an order fixed per query, so results do not depend on the kernel
 //    chosen, the workgroup size, the grid order, the number of heads or the
 //    strides.
-// The bf16 kernel runs one wavefront per SIMD and software-pipelines each
-// wavefront's key loop (matrix work of one tile interleaved with the softmax
-// work of its neighbour); it serves dense and block-sparse attention. fp32
-// inputs use v_mfma_f32_32x32x2_f32 with the same structure and P kept in
-// fp32.
+// Two bf16 kernels. Dense attention over a large grid runs eight
+// wavefronts per workgroup, two per SIMD, each a plain loop over the key
+// tiles: the SIMD overlaps one wavefront's softmax with the other's MFMAs.
+// Block-sparse attention (one 128-row mask row per workgroup) and dense
+// grids too small to fill the chip at 256 rows per workgroup run four
+// wavefronts, one per SIMD, each software-pipelining its key loop (matrix
+// work of one tile interleaved with the softmax work of its neighbour).
+// fp32 inputs use v_mfma_f32_32x32x2_f32 with the same structure and P kept
+// in fp32.
 #include "attn_common.hpp"
 
 #include <cstring>
@@ -430,6 +434,229 @@ __global__ __launch_bounds__(kSpWaves * 64, 1) void attn_fwd_bf16_sp_kernel(Attn
   }
 }
 
+// ------------------------------- bf16 dense, two wavefronts per SIMD (8 waves)
+//
+// Eight wavefronts of 32 query rows (256 rows per workgroup), two per SIMD,
+// each running the plain step per 64-key tile: S = K Q^T (16 MFMA), the
+// online softmax of S (same arithmetic, in the same order, as the pipelined
+// kernel above, so both give the same bits), then O^T += V^T P^T (16 MFMA).
+// Instead of software-pipelining one wavefront, the two wavefronts on a
+// SIMD fill each other's gaps: one runs its softmax on the VALU while the
+// other's MFMAs keep the matrix core busy. Sharing every K/V tile among 256
+// query rows also halves the tile traffic into LDS per query.
+//
+// K/V tiles use three LDS slots per tensor (96 KiB) and are loaded two
+// tiles ahead: step t waits for tile t+1 (tile t+2 may still be in flight),
+// meets the other wavefronts at one barrier (after which slot t is free)
+// and issues tile t+3 into it. The kernel fits 256 registers per
+// wavefront, which is what lets two wavefronts share a SIMD.
+
+constexpr int kW8Waves = 8;
+constexpr int kW8BM = kW8Waves * kQW;   // 256 query rows per workgroup
+constexpr int kW8Slots = 3;             // LDS slots per tensor
+// Smallest grid (in 256-row workgroups) the 8-wavefront kernel is used for:
+// two rounds over the 256 CUs.
+constexpr int64_t kW8MinItems = 512;
+
+__global__ __launch_bounds__(kW8Waves * 64, 1) void attn_fwd_bf16_w8_kernel(AttnParams p) {
+  constexpr int LPW = (kTileBytes / 1024) / kW8Waves;   // 1-KiB loads per wavefront per tensor
+  static_assert(LPW * kW8Waves * 1024 == kTileBytes, "tile/threads mismatch");
+
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k[kW8Slots][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_v[kW8Slots][kTileBytes];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const Item it = decode_item(xcd_remap(blockIdx.x, gridDim.x), p.n_qblk, p.H);
+  const int qi = it.qblk * kW8BM + wave * kQW + l32;
+  const bool q_ok = qi < p.Sq;
+  const __bf16* qp = static_cast<const __bf16*>(p.q) + it.b * p.q_sb + it.h * p.q_sh;
+  const __bf16* kp = static_cast<const __bf16*>(p.k) + it.b * p.k_sb + it.h * p.k_sh;
+  const __bf16* vp = static_cast<const __bf16*>(p.v) + it.b * p.v_sb + it.h * p.v_sh;
+  const int n_tiles = (p.Skv + kBN - 1) / kBN;
+
+  // Q fragments (B operand of S^T = K Q^T): lane holds Q[qi][16 s + 8 hh .. +7].
+  bf16x8 qf[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    qf[s] = q_ok ? *reinterpret_cast<const bf16x8*>(qp + (int64_t)qi * p.q_ss + 16 * s + 8 * hh)
+                 : bf16x8{};
+  // Q has landed before any tile load is issued. The compiler does not see
+  // the tile loads (inline asm), so a Q load it still thought in flight
+  // would make it wait on the vector-memory counter inside the key loop,
+  // which would also wait for the tiles prefetched ahead.
+  wait_vmcnt<0>();
+
+  // tile loads and LDS fragment reads: as in the pipelined kernel
+  const uint32_t k_rb = (uint32_t)(p.k_ss * 2), v_rb = (uint32_t)(p.v_ss * 2);
+  const int k_rec = (int)((uint32_t)(p.Skv - 1) * k_rb + kD * 2);
+  const int v_rec = (int)((uint32_t)(p.Skv - 1) * v_rb + kD * 2);
+  uint32_t koff[LPW], voff[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int r = 4 * (wave * LPW + j) + (lane >> 4);
+    const int pos = lane & 15;
+    koff[j] = (uint32_t)r * k_rb + ((uint32_t)swz_k(r, pos) << 4);
+    voff[j] = (uint32_t)r * v_rb + ((uint32_t)swz_v(r, pos) << 4);
+  }
+  auto kslot = [&](int slot) __device__ -> unsigned char* { return lds_k[slot]; };
+  auto vslot = [&](int slot) __device__ -> unsigned char* { return lds_v[slot]; };
+  const i32x4 k_rsrc = make_rsrc(kp, k_rec), v_rsrc = make_rsrc(vp, v_rec);
+  auto issue = [&](int t, int slot) __device__ {
+    const uint32_t bk = (uint32_t)t * kBN * k_rb, bv = (uint32_t)t * kBN * v_rb;
+    const uint32_t dk = lds_addr(kslot(slot)) + wave * LPW * 1024;
+    const uint32_t dv = lds_addr(vslot(slot)) + wave * LPW * 1024;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) lds_dma16(dk + j * 1024, koff[j] + bk, k_rsrc);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) lds_dma16(dv + j * 1024, voff[j] + bv, v_rsrc);
+  };
+  uint32_t kofs[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) kofs[s] = (uint32_t)(l32 * 256 + (swz_k(l32, 2 * s + hh) << 4));
+  uint32_t vofs[2][4];
+  tr_offsets(lane, vofs);
+  auto kread = [&](int slot, int i) __device__ -> bf16x8 {
+    const LDS_AS unsigned char* b = (LDS_AS const unsigned char*)kslot(slot);
+    return *(LDS_AS const bf16x8*)(b + kofs[i >> 1] + (i & 1) * 8192);
+  };
+  auto vread = [&](int slot, int i) __device__ -> bf16x8 { return tr_read(vslot(slot), vofs, i); };
+
+  const float c = p.scale_log2;
+  f32x16 acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
+  float m_run = kNegInf, mc = 0.0f, l_run = 0.0f;
+
+  // one key tile in slot `slot`
+  auto step = [&](int slot, int t) __device__ {
+    f32x16 st[2];
+    st[0] = f32x16{};
+    st[1] = f32x16{};
+    bf16x8 kf[16];
+    kf[0] = kread(slot, 0);
+    kf[1] = kread(slot, 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i + 2 < 16) kf[i + 2] = kread(slot, i + 2);
+      st[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i >> 1], st[i & 1], 0, 0, 0);
+    }
+    const int key0 = t * kBN;
+    if (key0 + kBN > p.Skv) {
+      const int lim = p.Skv - key0 - 4 * hh;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + (r & 3);
+        if (off >= lim) st[0][r] = kNegInf;
+        if (off + 32 >= lim) st[1][r] = kNegInf;
+      }
+    }
+    // row max -> lazy rescale -> x = exp2(s c - m c), l += x in key order,
+    // P = bf16(x)
+    float part_max = kNegInf;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) part_max = fmaxf(part_max, st[e >> 4][e & 15]);
+    const float mx = pair_max(part_max);
+    const bool need = (mx - m_run) * c > kRescaleLog2;
+    const float m_new = need ? mx : m_run;
+    const float alpha = need ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.0f;
+    const bool any_need = wave_any(need);
+    m_run = m_new;
+    mc = (m_run == kNegInf) ? 0.0f : m_run * c;
+    l_run *= alpha;
+    if (any_need) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) acc[db] *= alpha;
+    }
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(st[e >> 4][e & 15], c, -mc));
+      l_run = l_run + x;
+      pf[e >> 4][(e & 15) >> 3][e & 7] = (__bf16)x;
+    }
+    bf16x8 vf[16];
+    vf[0] = vread(slot, 0);
+    vf[1] = vread(slot, 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i + 2 < 16) vf[i + 2] = vread(slot, i + 2);
+      const int db = i & 3, jj = (i >> 2) & 1, kb = i >> 3;
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[kb][jj], acc[db], 0, 0, 0);
+    }
+  };
+  // after step t: tile t+1 landed for every wavefront, slot of tile t free
+  auto advance = [&](int slot, int t) __device__ {
+    if (t + 1 < n_tiles) {
+      if (t + 2 < n_tiles) wait_vmcnt<2 * LPW>();   // tile t+2 may stay in flight
+      else wait_vmcnt<0>();
+      barrier_no_fence();
+      if (t + 3 < n_tiles) issue(t + 3, slot);
+    }
+  };
+
+  issue(0, 0);
+  if (n_tiles > 2) {
+    issue(1, 1);
+    issue(2, 2);
+    wait_vmcnt<4 * LPW>();
+  } else if (n_tiles > 1) {
+    issue(1, 1);
+    wait_vmcnt<2 * LPW>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  barrier_no_fence();
+  // t is a multiple of 3 at the top of the loop, so every slot index is a
+  // compile-time constant
+  int t = 0;
+  for (; t + 3 <= n_tiles; t += 3) {
+    step(0, t);
+    advance(0, t);
+    step(1, t + 1);
+    advance(1, t + 1);
+    step(2, t + 2);
+    advance(2, t + 2);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (t < n_tiles) {
+      step(j, t);
+      advance(j, t);
+      ++t;
+    }
+  }
+
+  // ---- epilogue: combine halves, normalise, write O and LSE. The row's
+  // addresses are derived again here (from a copy of the thread id the
+  // compiler cannot match with the first), so that they do not occupy
+  // registers through the key loop.
+  const float l_tot = pair_sum(l_run);
+  int tid2 = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid2));
+  const Item it2 = decode_item(xcd_remap(blockIdx.x, gridDim.x), p.n_qblk, p.H);
+  const int qi2 = it2.qblk * kW8BM + (tid2 >> 6) * kQW + (tid2 & 31);
+  if (qi2 >= p.Sq) return;
+  float* op = p.o + it2.b * p.o_sb + it2.h * p.o_sh + (int64_t)qi2 * p.o_ss;
+  const bool empty = !(l_tot > 0.0f);
+  const float inv_l = empty ? 0.0f : 1.0f / l_tot;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = db * 32 + 8 * g4 + 4 * hh;
+      f32x4 o4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o4[i] = acc[db][4 * g4 + i] * inv_l;
+      *reinterpret_cast<f32x4*>(op + d) = o4;
+    }
+  if (hh == 0) {
+    const float lse = empty ? kNegInf : m_run * p.scale + __logf(l_tot);
+    p.lse[it2.b * p.lse_sb + it2.h * p.lse_sh + qi2] = lse;
+  }
+}
+
 // ------------------------------------------------------------------ f32 path
 
 // LDS row stride (floats) of the fp32 tiles: padded against bank conflicts.
@@ -606,6 +833,17 @@ hipError_t launch_attn_dense(const AttnParams& p0, DType dt, hipStream_t s) {
     p.n_qblk = (p.Sq + 127) / 128;
     p.n_items = p.B * p.H * p.n_qblk;
     hipLaunchKernelGGL((attn_fwd_f32_kernel<4, false>), dim3(p.n_items), dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
+  // Large grids: the 8-wavefront kernel (two wavefronts per SIMD). Small
+  // grids, which would leave CUs idle at 256 query rows per workgroup (a
+  // ring round of 4096 queries x 8 heads gives 128): the pipelined kernel.
+  // Both give the same bits.
+  const int64_t w8_items = (int64_t)p.B * p.H * ((p.Sq + kW8BM - 1) / kW8BM);
+  if (w8_items >= kW8MinItems) {
+    p.n_qblk = (p.Sq + kW8BM - 1) / kW8BM;
+    p.n_items = (int32_t)w8_items;
+    hipLaunchKernelGGL(attn_fwd_bf16_w8_kernel, dim3(p.n_items), dim3(kW8Waves * 64), 0, s, p);
     return hipGetLastError();
   }
   p.n_qblk = (p.Sq + kSpBM - 1) / kSpBM;

@@ -5,8 +5,14 @@ hipcc cross-compiles without a GPU).
   is only sound while nothing else in those kernels uses M0, so every M0
   access must be an `s_mov_b32 m0, sN` directly followed by the
   `buffer_load_dwordx4 ... lds` it serves.
-* The attention kernels must not spill to scratch: a spill in the key loop
-  costs far more than it saves.
+* The attention kernels must not touch scratch memory inside a loop: a
+  spill in the key loop costs far more than it saves. A few spilled words
+  outside the loops (values that live across the key loop but are not used
+  in it) cost nothing measurable and are allowed, up to 64 bytes.
+* Inside the loops, a wait on the vector-memory counter may only come right
+  before a barrier. The tile loads into LDS are inline asm the compiler does
+  not count, so a wait it inserts for a load it does see (say, of Q) would
+  also wait for the tiles loaded ahead.
 """
 import os
 import re
@@ -64,8 +70,52 @@ def test_m0_only_feeds_lds_loads(asm):
             assert nxt.startswith("buffer_load_dwordx4") and nxt.endswith(" lds"), (name, l, nxt)
 
 
-def test_attention_kernels_do_not_spill(asm):
+def _loops(lines):
+    """(header, back-edge) line ranges of the loops the compiler annotated."""
+    labels = {l.split(":")[0]: i for i, l in enumerate(lines) if re.match(r"^\.LBB\d+_\d+:", l)}
+    out = []
+    for i, l in enumerate(lines):
+        m = re.search(r"s_c?branch\S*\s+(\.LBB\d+_\d+)", l)
+        if m and m.group(1) in labels and labels[m.group(1)] < i and \
+                "Loop Header" in lines[labels[m.group(1)]]:
+            out.append((labels[m.group(1)], i))
+    return out
+
+
+def _attention_bodies(asm):
+    funcs = _functions(asm)
+    bodies = {n: b.split("\n") for n, b in funcs.items()
+              if re.search(r"attn_(fwd|bwd)\w*_kernel", n) and "empty" not in n}
+    assert bodies, "no attention kernels found"
+    return bodies
+
+
+def test_attention_kernels_do_not_spill_in_loops(asm):
     sizes = dict(re.findall(r"\.set (_ZN3lsh\S*attn_(?:fwd|bwd)\S*)\.private_seg_size, (\d+)", asm))
     assert sizes, "no attention kernels found"
     for name, size in sizes.items():
-        assert int(size) == 0, (name, size)
+        assert int(size) <= 64, (name, size)
+    for name, lines in _attention_bodies(asm).items():
+        for a, b in _loops(lines):
+            bad = [l.strip() for l in lines[a:b + 1] if "scratch_" in l or "buffer_store" in l]
+            assert not bad, (name, bad[:3])
+
+
+def test_vmcnt_waits_in_loops_only_before_barriers(asm):
+    for name, lines in _attention_bodies(asm).items():
+        loops = _loops(lines)
+        if re.search(r"bf16|dkdv|bwd_dq", name):   # the kernels with a key or query loop
+            assert loops, (name, "no loop found")
+        for a, b in loops:
+            code = [l.split(";")[0].strip() for l in lines[a:b + 1]]
+            code = [l for l in code if l]
+            for i, l in enumerate(code):
+                if l.startswith("s_waitcnt") and "vmcnt" in l:
+                    # the next instruction, skipping labels and the scalar
+                    # branch bookkeeping of the wait's own if/else, is the
+                    # barrier
+                    rest = [x for x in code[i + 1:i + 10]
+                            if not re.match(r"\.LBB\d+_\d+:", x) and not x.split()[0].startswith(
+                                ("s_branch", "s_cbranch", "s_mov_b64", "s_andn2_b64", "s_and_b64",
+                                 "s_waitcnt"))]
+                    assert rest and rest[0] == "s_barrier", (name, l, code[i + 1:i + 4])

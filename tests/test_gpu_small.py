@@ -156,9 +156,10 @@ def test_run_to_run_bit_identical(L):
 
 
 def test_workgroup_size_does_not_change_bits(L):
-    """Head 0 alone (128 workgroups) vs all 8 heads (1024 workgroups) and a
-    {1, 7} chunking vs the unchunked call: grid size and chunking must not
-    change a bit."""
+    """All 8 heads (512 workgroups of 256 rows: the eight-wavefront kernel)
+    vs a {1, 7} chunking and head 0 alone (grids of 128 and 896 rows-of-128
+    workgroups: the pipelined kernel): neither the kernel, the grid size nor
+    the chunking may change a bit."""
     G.announce("workgroup-size invariance")
     t = G.torch()
     S, H = 16384, 8
@@ -170,6 +171,42 @@ def test_workgroup_size_does_not_change_bits(L):
     assert t.equal(o1, o2) and t.equal(l1, l2)
     o3, l3 = L.attn_fwd(qg[:, :, :1].contiguous(), kg[:, :, :1].contiguous(), vg[:, :, :1].contiguous())
     assert t.equal(o1[:, :, :1], o3) and t.equal(l1[:, :1], l3)
+
+
+def test_eight_wave_kernel_strided(L):
+    """B=2, Sq=777 (last 256-row block holds 9 rows), Skv=333, H=64: 512
+    workgroups, so the eight-wavefront kernel runs, here on Q, K, V as views
+    of one packed [B, S, 3, H, D] buffer with O written into a wider one.
+    Four heads against the oracle on every row; every head bit-identical to
+    calls on 4 heads at a time (64-workgroup grids: the pipelined kernel)."""
+    G.announce("eight-wave kernel, strided")
+    t = G.torch()
+    B, Sq, Skv, H, D = 2, 777, 333, 64, 128
+    q, k, v = I.make_custom((B, Sq, H, D), (B, Skv, H, D), "bf16", seed=77)
+    qg = G.to_gpu(q, "bf16")
+    packed = t.zeros((B, Sq, 3, H, D), dtype=t.bfloat16, device="cuda")
+    packed[:, :, 0] = qg
+    packed[:, :Skv, 1] = G.to_gpu(k, "bf16")
+    packed[:, :Skv, 2] = G.to_gpu(v, "bf16")
+    qv, kv, vv = packed[:, :, 0], packed[:, :Skv, 1], packed[:, :Skv, 2]
+    wide = t.full((B, Sq, H + 2, D), float("nan"), dtype=t.float32, device="cuda")
+    o = wide[:, :, 1:H + 1]
+    lse = t.full((B, H, Sq), float("nan"), dtype=t.float32, device="cuda")
+    L.attn_fwd(qv, kv, vv, o=o, lse=lse)
+    heads = [0, 1, 37, 63]
+    o_ref, lse_ref = oracle.attention_ref(q.values, k.values, v.values, 1 / math.sqrt(D),
+                                          heads=heads)
+    sig = G.bf16_weight_sigma(oracle, q.values, k.values, v.values, 1 / math.sqrt(D), lse_ref,
+                              heads=heads)
+    og, lg = o.cpu().numpy(), lse.cpu().numpy()
+    G.check("eight-wave strided", "bf16", og[:, :, heads], lg[:, heads], o_ref[:, :, heads],
+            lse_ref[:, heads], sigma=sig[:, :, heads])
+    assert t.isnan(wide[:, :, 0]).all() and t.isnan(wide[:, :, H + 1]).all(), "wrote outside O"
+    assert not t.isnan(o).any() and not t.isnan(lse).any(), "unwritten output"
+    for h0 in range(0, H, 4):
+        sl = slice(h0, h0 + 4)
+        o4, l4 = L.attn_fwd(qv[:, :, sl], kv[:, :, sl], vv[:, :, sl])
+        assert t.equal(o[:, :, sl], o4) and t.equal(lse[:, sl], l4), f"heads {h0}..{h0 + 3}"
 
 
 def test_permute_bit_exact(L):
