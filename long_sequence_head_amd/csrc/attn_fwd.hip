@@ -32,13 +32,16 @@
 //    in an order fixed per query, so results do not depend on the kernel
 //    chosen, the workgroup size, the grid order, the number of heads or the
 //    strides.
-// Two bf16 kernels. Dense attention over a large grid runs eight
-// wavefronts per workgroup, two per SIMD, each a plain loop over the key
-// tiles: the SIMD overlaps one wavefront's softmax with the other's MFMAs.
-// Block-sparse attention (one 128-row mask row per workgroup) and dense
-// grids too small to fill the chip at 256 rows per workgroup run four
-// wavefronts, one per SIMD, each software-pipelining its key loop (matrix
-// work of one tile interleaved with the softmax work of its neighbour).
+// Three bf16 kernels, two wavefronts per SIMD where the grid allows:
+//  * dense, large grids: eight wavefronts per workgroup (256 query rows),
+//    one workgroup per CU, each wavefront a plain loop over the key tiles;
+//    the SIMD overlaps one wavefront's softmax with the other's MFMAs;
+//  * block-sparse: the same plain loop with four wavefronts (one 128-row
+//    mask row) and two workgroups per CU;
+//  * dense grids too small to fill the chip at 256 rows per workgroup (a
+//    ring round): four wavefronts, one per SIMD, each software-pipelining
+//    its key loop (matrix work of one tile interleaved with the softmax
+//    work of its neighbour).
 // fp32 inputs use v_mfma_f32_32x32x2_f32 with the same structure and P kept
 // in fp32.
 #include "attn_common.hpp"
@@ -104,9 +107,9 @@ __device__ __forceinline__ int tile_key0(int t, const unsigned short* kept) {
 //       row sum of x(t), the row max of S(t+1), the lazy-rescale decision and
 //       the scaling s c - m c of S(t+1).
 // Every query's arithmetic (product order, exp2 arguments, summation order,
-// rescale points, bf16 rounding of P) depends on its own scores only, so
-// dense and block-sparse launches, any grid and any head chunking give the
-// same bits.
+// rescale points, bf16 rounding of P) depends on its own scores only, and is
+// the same as in the plain kernels below, so every kernel, grid and head
+// chunking gives the same bits.
 //
 // K/V tiles go HBM -> LDS directly (buffer_load ... lds) into two slots per
 // tensor. Each slot is its own LDS variable and every access names its slot
@@ -123,51 +126,30 @@ __device__ __forceinline__ int tile_key0(int t, const unsigned short* kept) {
 constexpr int kSpWaves = 4;
 constexpr int kSpBM = kSpWaves * kQW;   // 128 query rows per workgroup
 
-template <bool SPARSE>
 __global__ __launch_bounds__(kSpWaves * 64, 1) void attn_fwd_bf16_sp_kernel(AttnParams p) {
   constexpr int LPW = (kTileBytes / 1024) / kSpWaves;   // 1-KiB loads per wavefront per tensor
   static_assert(LPW * kSpWaves * 1024 == kTileBytes, "tile/threads mismatch");
-  static_assert(!SPARSE || kSpBM == kMaskBlock, "a sparse workgroup covers one mask row");
 
   __shared__ __attribute__((aligned(1024))) unsigned char lds_k0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_k1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_v0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_v1[kTileBytes];
-  extern __shared__ unsigned short kept_dyn[];   // sparse: kept key blocks of the mask row
-  __shared__ int wave_cnt[kSpWaves];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
 
-  // Dense: workgroups walk the items XCD by XCD. Sparse: in the given order
-  // (most kept blocks first).
-  int item;
-  if constexpr (SPARSE) {
-    item = p.order ? p.order[blockIdx.x] : (int)blockIdx.x;
-  } else {
-    item = xcd_remap(blockIdx.x, gridDim.x);
-  }
-  const Item it = decode_item(item, p.n_qblk, p.H);
+  // workgroups walk the items XCD by XCD
+  const Item it = decode_item(xcd_remap(blockIdx.x, gridDim.x), p.n_qblk, p.H);
   const int qi = it.qblk * kSpBM + wave * kQW + l32;
   const bool q_ok = qi < p.Sq;
   const __bf16* qp = static_cast<const __bf16*>(p.q) + it.b * p.q_sb + it.h * p.q_sh;
   const __bf16* kp = static_cast<const __bf16*>(p.k) + it.b * p.k_sb + it.h * p.k_sh;
   const __bf16* vp = static_cast<const __bf16*>(p.v) + it.b * p.v_sb + it.h * p.v_sh;
 
-  // Key tiles: dense, 64-key tiles in order; sparse, the two 64-key halves
-  // of every kept 128-key block in ascending order, without a half that lies
-  // wholly past the last key. Either way only the last tile can be ragged.
-  int n_tiles;
-  if constexpr (SPARSE) {
-    const uint8_t* mrow = p.mask + (((int64_t)it.b * p.H + it.h) * p.n_mqb + it.qblk) * p.n_mkb;
-    const int n_kept = build_kept_list<kSpWaves * 64>(mrow, p.n_mkb, kept_dyn, wave_cnt);
-    n_tiles = 2 * n_kept;
-    if (n_kept > 0 && (int)kept_dyn[n_kept - 1] * kMaskBlock + kBN >= p.Skv) n_tiles -= 1;
-  } else {
-    n_tiles = (p.Skv + kBN - 1) / kBN;
-  }
-  auto key0_of = [&](int t) __device__ -> int { return tile_key0<SPARSE>(t, kept_dyn); };
+  // 64-key tiles in order; only the last can be ragged
+  const int n_tiles = (p.Skv + kBN - 1) / kBN;
+  auto key0_of = [&](int t) __device__ -> int { return t * kBN; };
 
   // Q fragments (B operand of S^T = K Q^T): lane holds Q[qi][16 s + 8 hh .. +7].
   bf16x8 qf[8];
@@ -434,22 +416,28 @@ __global__ __launch_bounds__(kSpWaves * 64, 1) void attn_fwd_bf16_sp_kernel(Attn
   }
 }
 
-// ------------------------------- bf16 dense, two wavefronts per SIMD (8 waves)
+// ------------------------- bf16, two wavefronts per SIMD, plain key loop
 //
-// Eight wavefronts of 32 query rows (256 rows per workgroup), two per SIMD,
-// each running the plain step per 64-key tile: S = K Q^T (16 MFMA), the
-// online softmax of S (same arithmetic, in the same order, as the pipelined
-// kernel above, so both give the same bits), then O^T += V^T P^T (16 MFMA).
-// Instead of software-pipelining one wavefront, the two wavefronts on a
-// SIMD fill each other's gaps: one runs its softmax on the VALU while the
-// other's MFMAs keep the matrix core busy. Sharing every K/V tile among 256
-// query rows also halves the tile traffic into LDS per query.
-//
-// K/V tiles use three LDS slots per tensor (96 KiB) and are loaded two
-// tiles ahead: step t waits for tile t+1 (tile t+2 may still be in flight),
-// meets the other wavefronts at one barrier (after which slot t is free)
-// and issues tile t+3 into it. The kernel fits 256 registers per
-// wavefront, which is what lets two wavefronts share a SIMD.
+// Each wavefront (32 query rows) runs the plain step per 64-key tile: S = K
+// Q^T (16 MFMA), the online softmax of S (same arithmetic, in the same
+// order, as the pipelined kernel above, so both give the same bits), then
+// O^T += V^T P^T (16 MFMA). Instead of software-pipelining one wavefront,
+// two wavefronts on a SIMD fill each other's gaps: one runs its softmax on
+// the VALU while the other's MFMAs keep the matrix core busy.
+//  * Dense (attn_fwd_bf16_w8_kernel): eight wavefronts and 256 query rows
+//    per workgroup, one workgroup per CU. Every K/V tile serves 256 rows,
+//    half the LDS fill per query of a 128-row workgroup. Three LDS slots per
+//    tensor (96 KiB), tiles loaded two ahead: step t waits for tile t+1
+//    (tile t+2 may still be in flight), meets the other wavefronts at one
+//    barrier (after which slot t is free) and issues tile t+3 into it.
+//  * Block-sparse (attn_fwd_bf16_w4s_kernel): four wavefronts on one
+//    128-row mask row, streaming the 64-key halves of its kept blocks in
+//    ascending order (without a half wholly past the last key, so only the
+//    last tile can be ragged). Two slots per tensor (64 KiB), tiles loaded
+//    one ahead, so that two workgroups, each with its own mask row, share a
+//    CU. A row without kept blocks gets O = 0 and LSE = -inf.
+// Both fit 256 registers per wavefront, which is what lets two wavefronts
+// share a SIMD.
 
 constexpr int kW8Waves = 8;
 constexpr int kW8BM = kW8Waves * kQW;   // 256 query rows per workgroup
@@ -457,24 +445,52 @@ constexpr int kW8Slots = 3;             // LDS slots per tensor
 // Smallest grid (in 256-row workgroups) the 8-wavefront kernel is used for:
 // two rounds over the 256 CUs.
 constexpr int64_t kW8MinItems = 512;
+// Block-sparse: 4 wavefronts (one 128-row mask row), two workgroups per CU
+// (their LDS, 2 x 64 KiB plus the kept-block lists, fits in 160 KiB).
+constexpr int kW4Waves = 4;
+constexpr int kW4Slots = 2;
 
-__global__ __launch_bounds__(kW8Waves * 64, 1) void attn_fwd_bf16_w8_kernel(AttnParams p) {
-  constexpr int LPW = (kTileBytes / 1024) / kW8Waves;   // 1-KiB loads per wavefront per tensor
-  static_assert(LPW * kW8Waves * 1024 == kTileBytes, "tile/threads mismatch");
+// The plain kernel body. WAVES wavefronts of 32 query rows; SLOTS LDS slots
+// per tensor, tiles loaded SLOTS-1 ahead.
+template <int WAVES, int SLOTS, bool SPARSE>
+__device__ __forceinline__ void plain_attention(const AttnParams& p) {
+  constexpr int BM = WAVES * kQW;
+  constexpr int LPW = (kTileBytes / 1024) / WAVES;   // 1-KiB loads per wavefront per tensor
+  constexpr int DIST = SLOTS - 1;                      // tiles loaded ahead
+  static_assert(LPW * WAVES * 1024 == kTileBytes, "tile/threads mismatch");
+  static_assert(!SPARSE || BM == kMaskBlock, "a sparse workgroup covers one mask row");
+  static_assert(DIST == 1 || DIST == 2, "one or two tiles ahead");
 
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_k[kW8Slots][kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_v[kW8Slots][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k[SLOTS][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_v[SLOTS][kTileBytes];
+  extern __shared__ unsigned short kept_dyn[];   // sparse: kept key blocks of the mask row
+  __shared__ int wave_cnt[WAVES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
-  const Item it = decode_item(xcd_remap(blockIdx.x, gridDim.x), p.n_qblk, p.H);
-  const int qi = it.qblk * kW8BM + wave * kQW + l32;
+  int item;
+  if constexpr (SPARSE) {
+    item = p.order ? p.order[blockIdx.x] : (int)blockIdx.x;
+  } else {
+    item = xcd_remap(blockIdx.x, gridDim.x);
+  }
+  const Item it = decode_item(item, p.n_qblk, p.H);
+  const int qi = it.qblk * BM + wave * kQW + l32;
   const bool q_ok = qi < p.Sq;
   const __bf16* qp = static_cast<const __bf16*>(p.q) + it.b * p.q_sb + it.h * p.q_sh;
   const __bf16* kp = static_cast<const __bf16*>(p.k) + it.b * p.k_sb + it.h * p.k_sh;
   const __bf16* vp = static_cast<const __bf16*>(p.v) + it.b * p.v_sb + it.h * p.v_sh;
-  const int n_tiles = (p.Skv + kBN - 1) / kBN;
+  int n_tiles;
+  if constexpr (SPARSE) {
+    const uint8_t* mrow = p.mask + (((int64_t)it.b * p.H + it.h) * p.n_mqb + it.qblk) * p.n_mkb;
+    const int n_kept = build_kept_list<WAVES * 64>(mrow, p.n_mkb, kept_dyn, wave_cnt);
+    n_tiles = 2 * n_kept;
+    if (n_kept > 0 && (int)kept_dyn[n_kept - 1] * kMaskBlock + kBN >= p.Skv) n_tiles -= 1;
+  } else {
+    n_tiles = (p.Skv + kBN - 1) / kBN;
+  }
+  auto key0_of = [&](int t) __device__ -> int { return tile_key0<SPARSE>(t, kept_dyn); };
 
   // Q fragments (B operand of S^T = K Q^T): lane holds Q[qi][16 s + 8 hh .. +7].
   bf16x8 qf[8];
@@ -504,7 +520,8 @@ __global__ __launch_bounds__(kW8Waves * 64, 1) void attn_fwd_bf16_w8_kernel(Attn
   auto vslot = [&](int slot) __device__ -> unsigned char* { return lds_v[slot]; };
   const i32x4 k_rsrc = make_rsrc(kp, k_rec), v_rsrc = make_rsrc(vp, v_rec);
   auto issue = [&](int t, int slot) __device__ {
-    const uint32_t bk = (uint32_t)t * kBN * k_rb, bv = (uint32_t)t * kBN * v_rb;
+    const uint32_t key0 = (uint32_t)key0_of(t);
+    const uint32_t bk = key0 * k_rb, bv = key0 * v_rb;
     const uint32_t dk = lds_addr(kslot(slot)) + wave * LPW * 1024;
     const uint32_t dv = lds_addr(vslot(slot)) + wave * LPW * 1024;
 #pragma unroll
@@ -542,7 +559,7 @@ __global__ __launch_bounds__(kW8Waves * 64, 1) void attn_fwd_bf16_w8_kernel(Attn
       if (i + 2 < 16) kf[i + 2] = kread(slot, i + 2);
       st[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i >> 1], st[i & 1], 0, 0, 0);
     }
-    const int key0 = t * kBN;
+    const int key0 = key0_of(t);
     if (key0 + kBN > p.Skv) {
       const int lim = p.Skv - key0 - 4 * hh;
 #pragma unroll
@@ -589,38 +606,51 @@ __global__ __launch_bounds__(kW8Waves * 64, 1) void attn_fwd_bf16_w8_kernel(Attn
   // after step t: tile t+1 landed for every wavefront, slot of tile t free
   auto advance = [&](int slot, int t) __device__ {
     if (t + 1 < n_tiles) {
-      if (t + 2 < n_tiles) wait_vmcnt<2 * LPW>();   // tile t+2 may stay in flight
-      else wait_vmcnt<0>();
+      if constexpr (DIST == 2) {
+        if (t + 2 < n_tiles) wait_vmcnt<2 * LPW>();   // tile t+2 may stay in flight
+        else wait_vmcnt<0>();
+      } else {
+        wait_vmcnt<0>();
+      }
       barrier_no_fence();
-      if (t + 3 < n_tiles) issue(t + 3, slot);
+      if (t + DIST + 1 < n_tiles) issue(t + DIST + 1, slot);
     }
   };
 
-  issue(0, 0);
-  if (n_tiles > 2) {
-    issue(1, 1);
-    issue(2, 2);
-    wait_vmcnt<4 * LPW>();
-  } else if (n_tiles > 1) {
-    issue(1, 1);
-    wait_vmcnt<2 * LPW>();
+  // prologue: the first DIST + 1 tiles, then wait for tile 0
+  if (n_tiles > 0) issue(0, 0);
+  if constexpr (DIST == 2) {
+    if (n_tiles > 2) {
+      issue(1, 1);
+      issue(2, 2);
+      wait_vmcnt<4 * LPW>();
+    } else if (n_tiles > 1) {
+      issue(1, 1);
+      wait_vmcnt<2 * LPW>();
+    } else {
+      wait_vmcnt<0>();
+    }
   } else {
-    wait_vmcnt<0>();
+    if (n_tiles > 1) {
+      issue(1, 1);
+      wait_vmcnt<2 * LPW>();
+    } else {
+      wait_vmcnt<0>();
+    }
   }
   barrier_no_fence();
-  // t is a multiple of 3 at the top of the loop, so every slot index is a
-  // compile-time constant
+  // t is a multiple of SLOTS at the top of the loop, so every slot index is
+  // a compile-time constant
   int t = 0;
-  for (; t + 3 <= n_tiles; t += 3) {
-    step(0, t);
-    advance(0, t);
-    step(1, t + 1);
-    advance(1, t + 1);
-    step(2, t + 2);
-    advance(2, t + 2);
+  for (; t + SLOTS <= n_tiles; t += SLOTS) {
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) {
+      step(j, t + j);
+      advance(j, t + j);
+    }
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < SLOTS - 1; ++j) {
     if (t < n_tiles) {
       step(j, t);
       advance(j, t);
@@ -635,8 +665,14 @@ __global__ __launch_bounds__(kW8Waves * 64, 1) void attn_fwd_bf16_w8_kernel(Attn
   const float l_tot = pair_sum(l_run);
   int tid2 = (int)threadIdx.x;
   asm volatile("" : "+v"(tid2));
-  const Item it2 = decode_item(xcd_remap(blockIdx.x, gridDim.x), p.n_qblk, p.H);
-  const int qi2 = it2.qblk * kW8BM + (tid2 >> 6) * kQW + (tid2 & 31);
+  int item2;
+  if constexpr (SPARSE) {
+    item2 = p.order ? p.order[blockIdx.x] : (int)blockIdx.x;
+  } else {
+    item2 = xcd_remap(blockIdx.x, gridDim.x);
+  }
+  const Item it2 = decode_item(item2, p.n_qblk, p.H);
+  const int qi2 = it2.qblk * BM + (tid2 >> 6) * kQW + (tid2 & 31);
   if (qi2 >= p.Sq) return;
   float* op = p.o + it2.b * p.o_sb + it2.h * p.o_sh + (int64_t)qi2 * p.o_ss;
   const bool empty = !(l_tot > 0.0f);
@@ -655,6 +691,14 @@ __global__ __launch_bounds__(kW8Waves * 64, 1) void attn_fwd_bf16_w8_kernel(Attn
     const float lse = empty ? kNegInf : m_run * p.scale + __logf(l_tot);
     p.lse[it2.b * p.lse_sb + it2.h * p.lse_sh + qi2] = lse;
   }
+}
+
+__global__ __launch_bounds__(kW8Waves * 64, 1) void attn_fwd_bf16_w8_kernel(AttnParams p) {
+  plain_attention<kW8Waves, kW8Slots, false>(p);
+}
+
+__global__ __launch_bounds__(kW4Waves * 64, 2) void attn_fwd_bf16_w4s_kernel(AttnParams p) {
+  plain_attention<kW4Waves, kW4Slots, true>(p);
 }
 
 // ------------------------------------------------------------------ f32 path
@@ -848,7 +892,7 @@ hipError_t launch_attn_dense(const AttnParams& p0, DType dt, hipStream_t s) {
   }
   p.n_qblk = (p.Sq + kSpBM - 1) / kSpBM;
   p.n_items = p.B * p.H * p.n_qblk;
-  hipLaunchKernelGGL(attn_fwd_bf16_sp_kernel<false>, dim3(p.n_items), dim3(kSpWaves * 64), 0, s, p);
+  hipLaunchKernelGGL(attn_fwd_bf16_sp_kernel, dim3(p.n_items), dim3(kSpWaves * 64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -860,7 +904,7 @@ hipError_t launch_attn_sparse(const AttnParams& p0, DType dt, hipStream_t s) {
   if (dt == DType::F32)
     hipLaunchKernelGGL((attn_fwd_f32_kernel<4, true>), dim3(p.n_items), dim3(256), dyn, s, p);
   else
-    hipLaunchKernelGGL(attn_fwd_bf16_sp_kernel<true>, dim3(p.n_items), dim3(kSpWaves * 64), dyn, s, p);
+    hipLaunchKernelGGL(attn_fwd_bf16_w4s_kernel, dim3(p.n_items), dim3(kW4Waves * 64), dyn, s, p);
   return hipGetLastError();
 }
 

@@ -342,6 +342,22 @@ def test_blocksparse_all_ones_equals_dense_bitwise(L):
     assert t.equal(o1, o2) and t.equal(l1, l2)
 
 
+def test_blocksparse_all_ones_large_grid_equals_dense_bitwise(L):
+    """H=32, S=4133: 1056 sparse workgroups, two to a CU, against the dense
+    call (544 workgroups of 256 rows: the eight-wavefront kernel); the last
+    key block holds 37 keys."""
+    G.announce("sparse all-ones, large grid")
+    t = G.torch()
+    S, H = 4133, 32
+    q, k, v = I.make_custom((1, S, H, 128), (1, S, H, 128), "bf16", seed=95)
+    qg, kg, vg = G.to_gpu(q, "bf16"), G.to_gpu(k, "bf16"), G.to_gpu(v, "bf16")
+    nb = -(-S // 128)
+    mask = t.ones((1, H, nb, nb), dtype=t.uint8, device="cuda")
+    o1, l1 = L.attn_fwd_blocksparse(qg, kg, vg, mask)
+    o2, l2 = L.attn_fwd(qg, kg, vg)
+    assert t.equal(o1, o2) and t.equal(l1, l2)
+
+
 def test_blocksparse_diagonal_is_blockwise_dense(L):
     G.announce("sparse diagonal")
     t = G.torch()
