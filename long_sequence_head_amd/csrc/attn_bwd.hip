@@ -17,18 +17,21 @@
 //           64-row query tile of the head through LDS. Per 32 queries:
 //           S = Q K^T and dP = dO V^T with keys in lanes, P and dS in
 //           registers, then dV^T += dO^T P and dK^T += Q^T dS.
-//  * dQ:    a workgroup owns 128 queries (Q and dO in registers) and
-//           streams 64-key tiles: S^T = K Q^T and dP^T = V dO^T with
+//  * dQ:    a workgroup owns 128 or 256 queries (Q and dO in registers)
+//           and streams 64-key tiles: S^T = K Q^T and dP^T = V dO^T with
 //           queries in lanes, then dQ^T += K^T dS^T.
 // S and dP are formed in both passes: 14 units of matrix work for the 10 of
 // the definition, in exchange for determinism without atomics and without a
 // quadratic dS buffer.
 //
-// Both streaming kernels run one wavefront per SIMD, keep three LDS slots
-// per streamed tensor and meet at one barrier per 64-row tile; the work of
-// a wavefront is software-pipelined over 32-row units (see the dK/dV
-// kernel). The dQ kernel lives in attn_bwd_dq.hip: it is compiled with its
-// MFMA results in VGPRs, while dK/dV keeps its 128 accumulators in AGPRs.
+// The dK/dV kernel runs one wavefront per SIMD, keeps three LDS slots per
+// streamed tensor and meets at one barrier per 64-row tile; the work of a
+// wavefront is software-pipelined over 32-row units. Its 128 accumulators
+// and K/V registers leave no room for a second wavefront per SIMD. The dQ
+// pass lives in attn_bwd_dq.hip, compiled with its MFMA results in VGPRs:
+// on large grids it runs eight wavefronts per workgroup, two per SIMD, each
+// in the plain order; on small grids a pipelined 4-wavefront kernel like
+// the dK/dV one.
 #include "attn_bwd_common.hpp"
 
 namespace lsh {

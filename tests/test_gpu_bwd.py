@@ -166,3 +166,27 @@ def test_bwd_head_independence(L):
     b = _grads(L, *part)
     for x, y in zip(a, b):
         assert t.equal(x[:, :, 1:3], y)
+
+
+def test_bwd_large_grid_dq(L):
+    """H=32, Sq=4133 (last 256-query block holds 37 rows), Skv=517: 544
+    workgroups of 256 queries, so dQ runs on the two-wavefronts-per-SIMD
+    kernel. Heads 0 and 31 against the oracle; every head bit-identical to
+    calls on 4 heads at a time (68 workgroups: the pipelined dQ kernel)."""
+    t = G.torch()
+    B, Sq, Skv, H = 1, 4133, 517, 32
+    G.announce("bwd large-grid dQ")
+    q, k, v = I.make_custom((B, Sq, H, 128), (B, Skv, H, 128), "bf16", seed=71)
+    do = I.make_custom_dout((B, Sq, H, 128), "bf16", seed=71)
+    full = [G.to_gpu(x, "bf16") for x in (q, k, v, do)]
+    got = _grads(L, *full)
+    heads = [0, 31]
+    ref = oracle.attention_bwd_ref(q.values, k.values, v.values, do.values, 1 / math.sqrt(128),
+                                   heads=heads)
+    G.check_grads("bwd large grid", [x[:, :, heads] for x in _np(got)],
+                  [r[:, :, heads] for r in ref])
+    for h0 in range(0, H, 4):
+        part = [x[:, :, h0:h0 + 4].contiguous() for x in full]
+        sub = _grads(L, *part)
+        for x, y in zip(got, sub):
+            assert t.equal(x[:, :, h0:h0 + 4], y), f"heads {h0}..{h0 + 3}"
