@@ -55,6 +55,9 @@ namespace {
 // Lazy-rescale threshold in log2 units: the running max is replaced only
 // when a new score exceeds it by more than this.
 constexpr float kRescaleLog2 = 8.0f;
+// A tile sum of exp2(s c - m c) within this bound proves every term below
+// 2^7, so no score can trigger the rescale (which needs a term above 2^8).
+constexpr float kSureSum = 128.0f;
 
 // Builds, in LDS, the ascending list of kept key blocks of one mask row.
 // Returns the number of kept blocks (same value in every thread).
@@ -569,29 +572,43 @@ __device__ __forceinline__ void plain_attention(const AttnParams& p) {
         if (off + 32 >= lim) st[1][r] = kNegInf;
       }
     }
-    // row max -> lazy rescale -> x = exp2(s c - m c), l += x in key order,
-    // P = bf16(x)
-    float part_max = kNegInf;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) part_max = fmaxf(part_max, st[e >> 4][e & 15]);
-    const float mx = pair_max(part_max);
-    const bool need = (mx - m_run) * c > kRescaleLog2;
-    const float m_new = need ? mx : m_run;
-    const float alpha = need ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.0f;
-    const bool any_need = wave_any(need);
-    m_run = m_new;
-    mc = (m_run == kNegInf) ? 0.0f : m_run * c;
-    l_run *= alpha;
-    if (any_need) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db) acc[db] *= alpha;
-    }
+    // x = exp2(s c - m c), l += x in key order, P = bf16(x), first with the
+    // running max as it stands. That is the lazy rescale's answer unless a
+    // score exceeds the max by more than 2^8 in probability, which needs a
+    // tile sum of x above 256; a sum within 128 (and a max already set)
+    // rules it out without the row max. Otherwise the row max is taken and
+    // the rescale decided as usual; if it fires, the exponentials are redone
+    // with the new max. Either way the values are those of the plain order.
+    const float l0 = l_run;
     bf16x8 pf[2][2];
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(st[e >> 4][e & 15], c, -mc));
       l_run = l_run + x;
       pf[e >> 4][(e & 15) >> 3][e & 7] = (__bf16)x;
+    }
+    const bool sure = m_run != kNegInf && l_run - l0 <= kSureSum;
+    if (wave_any(!sure)) {
+      float part_max = kNegInf;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) part_max = fmaxf(part_max, st[e >> 4][e & 15]);
+      const float mx = pair_max(part_max);
+      const bool need = (mx - m_run) * c > kRescaleLog2;
+      if (wave_any(need)) {
+        const float m_new = need ? mx : m_run;
+        const float alpha = need ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.0f;
+        m_run = m_new;
+        mc = (m_run == kNegInf) ? 0.0f : m_run * c;
+        l_run = l0 * alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) acc[db] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(st[e >> 4][e & 15], c, -mc));
+          l_run = l_run + x;
+          pf[e >> 4][(e & 15) >> 3][e & 7] = (__bf16)x;
+        }
+      }
     }
     bf16x8 vf[16];
     vf[0] = vread(slot, 0);

@@ -144,6 +144,48 @@ def test_monotone_scores(L, dtype, direction):
             lse_ref, sigma=sig)
 
 
+def test_rescale_paths_large_grid(L):
+    """Scores that rise along the keys at four rates, one per group of 16
+    heads (raw slope 1, 0.75 and 0.25 per key, and falling), plus a per-row
+    offset: the running max moves on every tile, every other tile, every
+    few tiles (with tile sums past the bound that skips the row max), or
+    never after the first. H=64 and Sq=2048 give 512 workgroups of 256
+    rows, so the eight-wavefront kernel runs; an all-ones block mask runs
+    the block-sparse kernel. Both must equal, bit for bit, calls on 4 heads
+    at a time (the pipelined kernel, which takes the row max of every
+    tile); heads 0, 20, 40 and 60 are checked against the oracle."""
+    G.announce("rescale paths, large grid")
+    t = G.torch()
+    B, Sq, Skv, H, D = 1, 2048, 1500, 64, 128
+    import lsh_inputs as II
+    rates = np.repeat(np.array([1.0, 0.75, 0.25, -1.0], np.float32), 16)
+    q = np.zeros((B, Sq, H, D), np.float32)
+    q[..., 0] = 8.0
+    q[..., 1] = np.linspace(-4, 4, Sq, dtype=np.float32)[None, :, None]
+    k = np.zeros((B, Skv, H, D), np.float32)
+    k[..., 0] = np.arange(Skv, dtype=np.float32)[None, :, None] / 8.0 * rates[None, None, :]
+    k[..., 1] = 1.0
+    q = II.bf16_bits_to_f32(II.bf16_bits(q))
+    k = II.bf16_bits_to_f32(II.bf16_bits(k))
+    _, _, v = I.make_custom((B, Sq, H, D), (B, Skv, H, D), "bf16", seed=37)
+    qg, kg, vg = G.values_to_gpu(q, "bf16"), G.values_to_gpu(k, "bf16"), G.to_gpu(v, "bf16")
+    o, lse = L.attn_fwd(qg, kg, vg)
+    nb = -(-Sq // 128), -(-Skv // 128)
+    o_s, lse_s = L.attn_fwd_blocksparse(qg, kg, vg, t.ones((B, H) + nb, dtype=t.uint8, device="cuda"))
+    assert t.equal(o, o_s) and t.equal(lse, lse_s), "block-sparse kernel differs"
+    for h0 in range(0, H, 4):
+        sl = slice(h0, h0 + 4)
+        o4, l4 = L.attn_fwd(qg[:, :, sl].contiguous(), kg[:, :, sl].contiguous(),
+                            vg[:, :, sl].contiguous())
+        assert t.equal(o[:, :, sl], o4) and t.equal(lse[:, sl], l4), f"heads {h0}..{h0 + 3}"
+    heads = [0, 20, 40, 60]
+    o_ref, lse_ref = oracle.attention_ref(q, k, v.values, 1 / math.sqrt(D), heads=heads)
+    sig = G.bf16_weight_sigma(oracle, q, k, v.values, 1 / math.sqrt(D), lse_ref, heads=heads)
+    og, lg = o.cpu().numpy(), lse.cpu().numpy()
+    G.check("rescale paths", "bf16", og[:, :, heads], lg[:, heads], o_ref[:, :, heads],
+            lse_ref[:, heads], sigma=sig[:, :, heads])
+
+
 def test_run_to_run_bit_identical(L):
     G.announce("run-to-run")
     t = G.torch()
