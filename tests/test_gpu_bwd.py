@@ -168,16 +168,18 @@ def test_bwd_head_independence(L):
         assert t.equal(x[:, :, 1:3], y)
 
 
-def test_bwd_large_grid_dq(L):
-    """H=32, Sq=4133 (last 256-query block holds 37 rows), Skv=517: 544
-    workgroups of 256 queries, so dQ runs on the two-wavefronts-per-SIMD
-    kernel. Heads 0 and 31 against the oracle; every head bit-identical to
-    calls on 4 heads at a time (68 workgroups: the pipelined dQ kernel)."""
+@pytest.mark.parametrize("Skv", [1, 65, 129, 517])
+def test_bwd_large_grid_dq(L, Skv):
+    """H=32, Sq=4133 (last 256-query block holds 37 rows): 544 workgroups
+    of 256 queries, so dQ runs on the two-wavefronts-per-SIMD kernel, over
+    1, 2, 3 and 9 key tiles (each load-ahead case, ragged last tiles).
+    Heads 0 and 31 against the oracle; every head bit-identical to calls on
+    4 heads at a time (68 workgroups: the pipelined dQ kernel)."""
     t = G.torch()
-    B, Sq, Skv, H = 1, 4133, 517, 32
-    G.announce("bwd large-grid dQ")
-    q, k, v = I.make_custom((B, Sq, H, 128), (B, Skv, H, 128), "bf16", seed=71)
-    do = I.make_custom_dout((B, Sq, H, 128), "bf16", seed=71)
+    B, Sq, H = 1, 4133, 32
+    G.announce(f"bwd large-grid dQ Skv={Skv}")
+    q, k, v = I.make_custom((B, Sq, H, 128), (B, Skv, H, 128), "bf16", seed=71 + Skv)
+    do = I.make_custom_dout((B, Sq, H, 128), "bf16", seed=71 + Skv)
     full = [G.to_gpu(x, "bf16") for x in (q, k, v, do)]
     got = _grads(L, *full)
     heads = [0, 31]
