@@ -8,7 +8,8 @@ B=1, S=56160, H=40, D=128, fp32 O + LSE, algorithmic TFLOP/s =
 4*B*H*S*S*D / time. One step = one lsh_attn_fwd over the whole input.
 Secondary workloads (same line, under "workloads"): the head-chunked
 two-stream pipeline at S=32760 ({16,12,12} chunks, permute included), the
-ring partials + LSE merge (Q 4096 tokens, 8 KV blocks of 4096, H=8), the
+ring partials + LSE merge (Q 4096 tokens, 8 KV blocks of 4096, H=8;
+also with each block folded into a running result on arrival), the
 block-sparse workload (S=32768, 128x128 mask, per-head density
 U[0.1,0.6)), the small fp32 case (B=4, S=128, H=32) and the backward
 (dQ, dK, dV) of the dense forward at S=32760, H=40. Inputs are the seeded
@@ -151,8 +152,19 @@ def bench_ring(L, I, w, steps, warmup):
     def step():
         partials()
         L.lse_merge(o_parts, l_parts, o=o, lse=lse)
+
+    o_run = torch.empty_like(o)
+    l_run = torch.empty_like(lse)
+
+    def step_online():
+        # each block folded into the running result as it arrives
+        o_run.zero_()
+        l_run.fill_(float("-inf"))
+        for i in range(n):
+            L.attn_partial_accumulate(qg, kb[i], vb[i], o_run, l_run)
     ms_step, _ = timed(step, steps, warmup)
     ms_part, _ = timed(partials, steps, warmup)
+    ms_online, _ = timed(step_online, steps, warmup)
     # merge from HBM: flush L2 and the Infinity Cache before each timed call
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     times = []
@@ -169,9 +181,11 @@ def bench_ring(L, I, w, steps, warmup):
     flops = 4 * w.B * w.H * w.Sq * w.Skv * w.D
     mbytes = (o_parts.numel() + l_parts.numel() + o.numel() + lse.numel()) * 4
     r = dict(step_ms=ms_step, partials_ms=ms_part, partials_tflops=flops / ms_part / 1e9,
-             merge_ms=ms_merge, merge_GBs=mbytes / ms_merge / 1e6, merge_bytes=mbytes)
+             merge_ms=ms_merge, merge_GBs=mbytes / ms_merge / 1e6, merge_bytes=mbytes,
+             online_step_ms=ms_online, online_step_tflops=flops / ms_online / 1e9)
     log(f"[bench] workload {w.wid}: step {ms_step:.3f} ms, 8 partials {ms_part:.3f} ms "
-        f"({r['partials_tflops']:.1f} TFLOP/s), merge {ms_merge * 1e3:.1f} us ({r['merge_GBs']:.0f} GB/s)")
+        f"({r['partials_tflops']:.1f} TFLOP/s), merge {ms_merge * 1e3:.1f} us ({r['merge_GBs']:.0f} GB/s); "
+        f"step folding each block on arrival {ms_online:.3f} ms ({r['online_step_tflops']:.1f} TFLOP/s)")
     return r
 
 

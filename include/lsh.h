@@ -160,6 +160,23 @@ size_t lsh_attn_fwd_chunked_workspace(const lsh_attn_args* args);
 lsh_status lsh_attn_partial(const lsh_attn_args* args, lsh_stream stream);
 
 /*
+ * One Ring Attention round folded into a running result (same page and
+ * section as lsh_attn_partial; the per-block results are combined as they
+ * arrive rather than all at the end). On entry o and lse hold attention
+ * over the key blocks folded in so far: O normalised over their keys, LSE
+ * their log-sum-exp; before the first block, O = 0 and LSE = -inf. On
+ * return they hold attention over those blocks and this one, merged row by
+ * row as lsh_lse_merge merges two parts (a row whose two LSE are both -inf
+ * is left as it is). Folding a block into O = 0, LSE = -inf gives exactly
+ * lsh_attn_partial's result for it. Arguments as for lsh_attn_partial;
+ * Skv = 0 returns LSH_OK and leaves o and lse untouched. o and lse are read
+ * and written in place: nothing else may use them until the call's work on
+ * the stream has finished, and the call must not overlap another that
+ * writes them.
+ */
+lsh_status lsh_attn_partial_accumulate(const lsh_attn_args* args, lsh_stream stream);
+
+/*
  * Merge n partial results over disjoint key sets (same page as above; the
  * "Re-Merge" of "CHARM+: Cross-Hardware Attention with Re-Merge Multistream
  * Mechanism", read as this merge):

@@ -12,6 +12,7 @@ Functions:
                       of each chunk on a second stream, overlapped with
                       the previous chunk's attention)
   attn_partial        attention against one KV block (a Ring round)
+  attn_partial_accumulate  one KV block folded into a running (O, LSE)
   lse_merge           merge of per-block partial results
   head_permute        [B, S, H, D] -> [B, hc, S, D] copy of heads [h0, h0+hc)
   attn_fwd_blocksparse  attention restricted to a 128x128 block mask
@@ -29,7 +30,8 @@ import math
 from . import _lib
 from ._lib import LshError, load  # noqa: F401
 
-__all__ = ["attn_fwd", "attn_fwd_chunked", "attn_partial", "lse_merge", "head_permute",
+__all__ = ["attn_fwd", "attn_fwd_chunked", "attn_partial", "attn_partial_accumulate",
+           "lse_merge", "head_permute",
            "attn_fwd_blocksparse", "attn_bwd", "bwd_workspace_bytes",
            "chunked_workspace_bytes", "blocksparse_workspace_bytes",
            "LshError", "load", "MASK_BLOCK"]
@@ -129,6 +131,20 @@ def attn_partial(q, k, v, scale=None, o=None, lse=None, stream=None):
     empty = k is None or k.shape[1] == 0
     a = _args(q, None if empty else k, None if empty else v, o, lse, scale)
     _lib.check("lsh_attn_partial", lib.lsh_attn_partial(ctypes.byref(a), _stream_ptr(stream)))
+    return o, lse
+
+
+def attn_partial_accumulate(q, k, v, o, lse, scale=None, stream=None):
+    """Fold attention against one KV block into a running result, in
+    place: o, lse hold attention over the blocks folded so far (O = 0,
+    LSE = -inf before the first) and afterwards over those and this one.
+    k and v may hold zero keys (nothing changes). Returns (o, lse)."""
+    lib = load()
+    o, lse = _outputs(q, o, lse)
+    empty = k is None or k.shape[1] == 0
+    a = _args(q, None if empty else k, None if empty else v, o, lse, scale)
+    _lib.check("lsh_attn_partial_accumulate",
+               lib.lsh_attn_partial_accumulate(ctypes.byref(a), _stream_ptr(stream)))
     return o, lse
 
 

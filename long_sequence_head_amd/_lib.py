@@ -54,6 +54,7 @@ SIGNATURES = {
                                             ctypes.c_size_t, c_vp, c_vp]),
     "lsh_attn_fwd_chunked_workspace": (ctypes.c_size_t, [_ARGS_P]),
     "lsh_attn_partial": (ctypes.c_int, [_ARGS_P, c_vp]),
+    "lsh_attn_partial_accumulate": (ctypes.c_int, [_ARGS_P, c_vp]),
     "lsh_lse_merge": (ctypes.c_int, [c_vp, c_vp, c_i32, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp]),
     "lsh_head_permute": (ctypes.c_int, [c_vp, c_vp, c_i32, c_i64, c_i64, c_i64, c_i64, c_i32, c_i32, c_vp]),
     "lsh_attn_fwd_blocksparse": (ctypes.c_int, [_ARGS_P, c_vp, c_vp, ctypes.c_size_t, c_vp]),

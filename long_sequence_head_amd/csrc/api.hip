@@ -287,6 +287,19 @@ lsh_status lsh_attn_partial(const lsh_attn_args* args, lsh_stream stream) {
                     "lsh_attn_partial");
 }
 
+lsh_status lsh_attn_partial_accumulate(const lsh_attn_args* args, lsh_stream stream) {
+  const char* fn = "lsh_attn_partial_accumulate";
+  lsh_status st = validate_attn(args, true, fn);
+  if (st != LSH_OK) return st;
+  if ((st = device_check_impl()) != LSH_OK) return st;
+  if (args->Skv == 0) return ok();   // an empty block leaves the running result as it is
+  lsh::AttnParams p = make_params(args);
+  p.accumulate = 1;
+  return hip_status(lsh::launch_attn_dense(p, static_cast<lsh::DType>(args->dtype),
+                                           static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 size_t lsh_attn_fwd_chunked_workspace(const lsh_attn_args* args) {
   if (validate_attn(args, false, "lsh_attn_fwd_chunked_workspace") != LSH_OK) return 0;
   const size_t one = (size_t)args->B * args->H * args->Sq * args->D * elem_bytes(args->dtype);

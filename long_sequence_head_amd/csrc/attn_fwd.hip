@@ -59,6 +59,55 @@ constexpr float kRescaleLog2 = 8.0f;
 // 2^7, so no score can trigger the rescale (which needs a term above 2^8).
 constexpr float kSureSum = 128.0f;
 
+// Writes a query row's O (this lane's half: head_dim 32 db + 8 g4 + 4 hh
+// .. +3, from the accumulator acc and the row sum l_tot) and, from the lane
+// with hh = 0, its LSE. With p.accumulate set, the row's (O, LSE) so far is
+// read first and merged with this key block's, as two parts of a key
+// partition merge:
+//   M = max(LSE_old, LSE_new), w = exp(LSE - M), Z = w_old + w_new,
+//   O = (w_old O_old + w_new O_new) / Z, LSE = M + log Z;
+// a row whose two LSE are both -inf is left as it is. Each lane reads only
+// the O chunks it writes, and both lanes of a row read the LSE before
+// either writes it (one load instruction for the wavefront).
+__device__ __forceinline__ void store_row(const AttnParams& p, float* op, float* lsep, int hh,
+                                          float l_tot, float m_run, const f32x16 (&acc)[4]) {
+  const bool empty = !(l_tot > 0.0f);
+  const float inv_l = empty ? 0.0f : 1.0f / l_tot;
+  const float lse = empty ? kNegInf : m_run * p.scale + __logf(l_tot);
+  if (!p.accumulate) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + 8 * g4 + 4 * hh;
+        f32x4 o4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o4[i] = acc[db][4 * g4 + i] * inv_l;
+        *reinterpret_cast<f32x4*>(op + d) = o4;
+      }
+    if (hh == 0) *lsep = lse;
+    return;
+  }
+  const float lse_old = *lsep;
+  const float mx = fmaxf(lse_old, lse);
+  if (mx == kNegInf) return;
+  const float w_old = __expf(lse_old - mx), w_new = __expf(lse - mx);
+  const float z = w_old + w_new;
+  const float a_old = w_old / z, a_new = w_new / z * inv_l;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = db * 32 + 8 * g4 + 4 * hh;
+      const f32x4 old = *reinterpret_cast<const f32x4*>(op + d);
+      f32x4 o4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o4[i] = __builtin_fmaf(acc[db][4 * g4 + i], a_new, old[i] * a_old);
+      *reinterpret_cast<f32x4*>(op + d) = o4;
+    }
+  if (hh == 0) *lsep = mx + __logf(z);
+}
+
 // Builds, in LDS, the ascending list of kept key blocks of one mask row.
 // Returns the number of kept blocks (same value in every thread).
 template <int NT>
@@ -400,23 +449,8 @@ __global__ __launch_bounds__(kSpWaves * 64, 1) void attn_fwd_bf16_sp_kernel(Attn
   // ---- epilogue: combine halves, normalise, write O and LSE
   const float l_tot = pair_sum(l_run);
   if (!q_ok) return;
-  float* op = p.o + it.b * p.o_sb + it.h * p.o_sh + (int64_t)qi * p.o_ss;
-  const bool empty = !(l_tot > 0.0f);
-  const float inv_l = empty ? 0.0f : 1.0f / l_tot;
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = db * 32 + 8 * g4 + 4 * hh;
-      f32x4 o4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o4[i] = acc[db][4 * g4 + i] * inv_l;
-      *reinterpret_cast<f32x4*>(op + d) = o4;
-    }
-  if (hh == 0) {
-    const float lse = empty ? kNegInf : m_run * p.scale + __logf(l_tot);
-    p.lse[it.b * p.lse_sb + it.h * p.lse_sh + qi] = lse;
-  }
+  store_row(p, p.o + it.b * p.o_sb + it.h * p.o_sh + (int64_t)qi * p.o_ss,
+            p.lse + it.b * p.lse_sb + it.h * p.lse_sh + qi, hh, l_tot, m_run, acc);
 }
 
 // ------------------------- bf16, two wavefronts per SIMD, plain key loop
@@ -691,23 +725,8 @@ __device__ __forceinline__ void plain_attention(const AttnParams& p) {
   const Item it2 = decode_item(item2, p.n_qblk, p.H);
   const int qi2 = it2.qblk * BM + (tid2 >> 6) * kQW + (tid2 & 31);
   if (qi2 >= p.Sq) return;
-  float* op = p.o + it2.b * p.o_sb + it2.h * p.o_sh + (int64_t)qi2 * p.o_ss;
-  const bool empty = !(l_tot > 0.0f);
-  const float inv_l = empty ? 0.0f : 1.0f / l_tot;
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = db * 32 + 8 * g4 + 4 * hh;
-      f32x4 o4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o4[i] = acc[db][4 * g4 + i] * inv_l;
-      *reinterpret_cast<f32x4*>(op + d) = o4;
-    }
-  if (hh == 0) {
-    const float lse = empty ? kNegInf : m_run * p.scale + __logf(l_tot);
-    p.lse[it2.b * p.lse_sb + it2.h * p.lse_sh + qi2] = lse;
-  }
+  store_row(p, p.o + it2.b * p.o_sb + it2.h * p.o_sh + (int64_t)qi2 * p.o_ss,
+            p.lse + it2.b * p.lse_sb + it2.h * p.lse_sh + qi2, hh, l_tot, m_run, acc);
 }
 
 __global__ __launch_bounds__(kW8Waves * 64, 1) void attn_fwd_bf16_w8_kernel(AttnParams p) {
@@ -852,23 +871,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_f32_kernel(AttnParams p) 
 
   const float l_tot = pair_sum(l_run);
   if (!q_ok) return;
-  float* op = p.o + it.b * p.o_sb + it.h * p.o_sh + (int64_t)qi * p.o_ss;
-  const bool empty = !(l_tot > 0.0f);
-  const float inv_l = empty ? 0.0f : 1.0f / l_tot;
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = db * 32 + 8 * g4 + 4 * hh;
-      f32x4 o4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o4[i] = acc[db][4 * g4 + i] * inv_l;
-      *reinterpret_cast<f32x4*>(op + d) = o4;
-    }
-  if (hh == 0) {
-    const float lse = empty ? kNegInf : m_run * p.scale + __logf(l_tot);
-    p.lse[it.b * p.lse_sb + it.h * p.lse_sh + qi] = lse;
-  }
+  store_row(p, p.o + it.b * p.o_sb + it.h * p.o_sh + (int64_t)qi * p.o_ss,
+            p.lse + it.b * p.lse_sb + it.h * p.lse_sh + qi, hh, l_tot, m_run, acc);
 }
 
 // O = 0, LSE = -inf for every row (attention over an empty key set).

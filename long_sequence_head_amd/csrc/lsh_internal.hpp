@@ -36,6 +36,9 @@ struct AttnParams {
   const uint8_t* mask;      // [B, H, n_mqb, n_mkb]
   int32_t n_mqb, n_mkb;
   const int32_t* order;     // work order over items, or nullptr
+  // nonzero: merge into the (O, LSE) already in o / lse (one ring round
+  // folded into a running result) instead of overwriting them
+  int32_t accumulate;
 };
 
 enum class DType : int { F32 = 0, BF16 = 1 };

@@ -109,6 +109,7 @@ def test_null_args_pointer():
     lib = _lib_or_skip()
     assert lib.lsh_attn_fwd(None, None) == _lib.LSH_ERR_INVALID
     assert lib.lsh_attn_partial(None, None) == _lib.LSH_ERR_INVALID
+    assert lib.lsh_attn_partial_accumulate(None, None) == _lib.LSH_ERR_INVALID
     assert lib.lsh_attn_fwd_chunked_workspace(None) == 0
     assert lib.lsh_attn_fwd_blocksparse_workspace(None) == 0
 
@@ -127,6 +128,7 @@ def test_valid_args_without_device_report_no_device():
     a = _valid_args()
     assert _call_fwd(lib, a) == _lib.LSH_ERR_NO_DEVICE
     assert lib.lsh_attn_partial(ctypes.byref(a), None) == _lib.LSH_ERR_NO_DEVICE
+    assert lib.lsh_attn_partial_accumulate(ctypes.byref(a), None) == _lib.LSH_ERR_NO_DEVICE
     assert lib.lsh_device_check() == _lib.LSH_ERR_NO_DEVICE
 
 
@@ -136,6 +138,8 @@ def test_partial_allows_empty_block():
     a.k = a.v = None
     st = lib.lsh_attn_partial(ctypes.byref(a), None)
     assert st in (_lib.LSH_OK, _lib.LSH_ERR_NO_DEVICE)   # valid arguments
+    st = lib.lsh_attn_partial_accumulate(ctypes.byref(a), None)
+    assert st in (_lib.LSH_OK, _lib.LSH_ERR_NO_DEVICE)
     assert lib.lsh_attn_fwd(ctypes.byref(a), None) == _lib.LSH_ERR_INVALID
 
 

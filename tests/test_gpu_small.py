@@ -312,6 +312,66 @@ def test_partial_and_merge_small(L, dtype):
             tol_o=1e-5, tol_lse=1e-5)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_partial_accumulate_small(L, dtype):
+    """The same uneven KV split (incl. an empty block) folded block by block
+    into a running (O, LSE) that starts at O = 0, LSE = -inf: against the
+    oracle's full attention, against the oracle merge of the same blocks'
+    partials, and the first fold bit-identical to lsh_attn_partial. Folding
+    an empty block leaves even a NaN-filled (O, LSE) untouched."""
+    G.announce(f"partial accumulate {dtype}")
+    t = G.torch()
+    B, Sq, Skv, H = 1, 300, 1000, 3
+    q, k, v = I.make_custom((B, Sq, H, 128), (B, Skv, H, 128), dtype, seed=61)
+    qg, kg, vg = G.to_gpu(q, dtype), G.to_gpu(k, dtype), G.to_gpu(v, dtype)
+    cuts = [0, 1, 64, 64, 500, 1000]
+    o = t.zeros((B, Sq, H, 128), dtype=t.float32, device="cuda")
+    lse = t.full((B, H, Sq), float("-inf"), dtype=t.float32, device="cuda")
+    parts = []
+    for i, (a, b) in enumerate(zip(cuts[:-1], cuts[1:])):
+        parts.append(L.attn_partial(qg, kg[:, a:b], vg[:, a:b]))
+        L.attn_partial_accumulate(qg, kg[:, a:b], vg[:, a:b], o, lse)
+        if i == 0:
+            assert t.equal(o, parts[0][0]) and t.equal(lse, parts[0][1]), "first fold"
+    o_ref, lse_ref = oracle.attention_ref(q.values, k.values, v.values, 1 / math.sqrt(128))
+    G.check(f"accumulate-vs-full {dtype}", dtype, o.cpu().numpy(), lse.cpu().numpy(), o_ref,
+            lse_ref)
+    om, lm = oracle.merge_ref(np.stack([p[0].cpu().numpy() for p in parts]),
+                              np.stack([p[1].cpu().numpy() for p in parts]))
+    G.check(f"accumulate-vs-oracle-merge {dtype}", dtype, o.cpu().numpy(), lse.cpu().numpy(), om,
+            lm, tol_o=1e-5, tol_lse=1e-5)
+    on, ln = G.poisoned_outputs(B, Sq, H)
+    L.attn_partial_accumulate(qg, kg[:, :0], vg[:, :0], on, ln)
+    t.cuda.synchronize()
+    assert t.isnan(on).all() and t.isnan(ln).all(), "an empty block changed the result"
+
+
+def test_partial_accumulate_large_grid(L):
+    """H=32, Sq=4133: each fold is a 544-workgroup launch of the
+    eight-wavefront kernel. Three blocks (1500, 1500, 37 keys) against the
+    oracle on heads 0 and 31; the first fold bit-identical to
+    lsh_attn_partial."""
+    G.announce("partial accumulate, large grid")
+    t = G.torch()
+    B, Sq, Skv, H = 1, 4133, 3037, 32
+    q, k, v = I.make_custom((B, Sq, H, 128), (B, Skv, H, 128), "bf16", seed=67)
+    qg, kg, vg = G.to_gpu(q, "bf16"), G.to_gpu(k, "bf16"), G.to_gpu(v, "bf16")
+    o = t.zeros((B, Sq, H, 128), dtype=t.float32, device="cuda")
+    lse = t.full((B, H, Sq), float("-inf"), dtype=t.float32, device="cuda")
+    cuts = [0, 1500, 3000, 3037]
+    for i, (a, b) in enumerate(zip(cuts[:-1], cuts[1:])):
+        L.attn_partial_accumulate(qg, kg[:, a:b], vg[:, a:b], o, lse)
+        if i == 0:
+            o1, l1 = L.attn_partial(qg, kg[:, a:b], vg[:, a:b])
+            assert t.equal(o, o1) and t.equal(lse, l1), "first fold"
+    heads = [0, 31]
+    o_ref, lse_ref = oracle.attention_ref(q.values, k.values, v.values, 1 / math.sqrt(128),
+                                          heads=heads)
+    og, lg = o.cpu().numpy(), lse.cpu().numpy()
+    G.check("accumulate large grid", "bf16", og[:, :, heads], lg[:, heads], o_ref[:, :, heads],
+            lse_ref[:, heads])
+
+
 @pytest.mark.parametrize("n", [1, 8, 9, 17])
 def test_merge_counts_vs_oracle(L, n):
     """n partials (one, exactly one group of 8, and counts that leave a
