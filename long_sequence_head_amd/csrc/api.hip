@@ -34,6 +34,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr int kMaxDevices = 64;
 std::mutex g_dev_mu;
 int g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+int g_dev_cus[kMaxDevices];    // compute units of each checked device
+// compute units of the device the calling thread's last successful device
+// check found (the kernels' grid-size choices use it)
+thread_local int g_cur_cus = 0;
 
 lsh_status device_check_impl() {
   int dev = -1;
@@ -50,8 +54,10 @@ lsh_status device_check_impl() {
       return fail(LSH_ERR_NO_DEVICE, "cannot query device %d", dev);
     }
     g_dev_state[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_dev_cus[dev] = prop.multiProcessorCount;
   }
   if (g_dev_state[dev] != 1) return fail(LSH_ERR_NO_DEVICE, "device %d is not gfx950", dev);
+  g_cur_cus = g_dev_cus[dev];
   return LSH_OK;
 }
 
@@ -138,6 +144,7 @@ lsh::AttnParams make_params(const lsh_attn_args* a) {
   p.Skv = (int32_t)a->Skv;
   p.scale = a->scale;
   p.scale_log2 = (float)((double)a->scale * 1.4426950408889634);  // scale * log2(e)
+  p.n_cu = g_cur_cus;
   return p;
 }
 
@@ -221,6 +228,7 @@ lsh::BwdParams make_bwd_params(const lsh_attn_bwd_args* a, void* workspace) {
   p.scale = a->scale;
   p.scale_log2 = (float)((double)a->scale * 1.4426950408889634);  // scale * log2(e)
   p.n_qt = (int32_t)((a->Sq + lsh::kBwdQT - 1) / lsh::kBwdQT);
+  p.n_cu = g_cur_cus;
   return p;
 }
 

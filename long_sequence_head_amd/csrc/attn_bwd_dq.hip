@@ -1,7 +1,8 @@
 // dQ pass of the attention backward (gfx950); the other passes and the
-// definitions are in attn_bwd.hip. Two kernels with the same bits: grids of
-// at least 512 workgroups of 256 queries run attn_bwd_dq8_kernel (two
-// wavefronts per SIMD), smaller grids the pipelined attn_bwd_dq_kernel.
+// definitions are in attn_bwd.hip. Two kernels with the same bits:
+// attn_bwd_dq8_kernel (two wavefronts per SIMD, 256 queries per workgroup)
+// unless its grid would leave CUs idle where the pipelined
+// attn_bwd_dq_kernel's (128 queries per workgroup) would not.
 #include "attn_bwd_common.hpp"
 
 namespace lsh {
@@ -225,9 +226,6 @@ __global__ __launch_bounds__(kBwdWaves * 64, 1) void attn_bwd_dq_kernel(BwdParam
 constexpr int kDq8Waves = 8;
 constexpr int kDq8Blk = kDq8Waves * 32;
 constexpr int kDq8Slots = 3;
-// smallest grid (in 256-query workgroups) it is used for: two rounds over
-// the 256 CUs
-constexpr int64_t kDq8MinItems = 512;
 
 __global__ __launch_bounds__(kDq8Waves * 64, 1) void attn_bwd_dq8_kernel(BwdParams p) {
   constexpr int LPW = (kTileBytes / 1024) / kDq8Waves;
@@ -410,7 +408,7 @@ __global__ __launch_bounds__(kDq8Waves * 64, 1) void attn_bwd_dq8_kernel(BwdPara
 hipError_t launch_attn_bwd_dq(const BwdParams& p, hipStream_t s) {
   const int64_t bh = (int64_t)p.B * p.H;
   const int64_t n8 = bh * ((p.Sq + kDq8Blk - 1) / kDq8Blk);
-  if (n8 >= kDq8MinItems) {
+  if (prefer_two_waves(n8, bh * ((p.Sq + kBwdBlk - 1) / kBwdBlk), p.n_cu)) {
     hipLaunchKernelGGL(attn_bwd_dq8_kernel, dim3((unsigned)n8), dim3(kDq8Waves * 64), 0, s, p);
     return hipGetLastError();
   }

@@ -479,9 +479,6 @@ __global__ __launch_bounds__(kSpWaves * 64, 1) void attn_fwd_bf16_sp_kernel(Attn
 constexpr int kW8Waves = 8;
 constexpr int kW8BM = kW8Waves * kQW;   // 256 query rows per workgroup
 constexpr int kW8Slots = 3;             // LDS slots per tensor
-// Smallest grid (in 256-row workgroups) the 8-wavefront kernel is used for:
-// two rounds over the 256 CUs.
-constexpr int64_t kW8MinItems = 512;
 // Block-sparse: 4 wavefronts (one 128-row mask row), two workgroups per CU
 // (their LDS, 2 x 64 KiB plus the kept-block lists, fits in 160 KiB).
 constexpr int kW4Waves = 4;
@@ -900,12 +897,13 @@ hipError_t launch_attn_dense(const AttnParams& p0, DType dt, hipStream_t s) {
     hipLaunchKernelGGL((attn_fwd_f32_kernel<4, false>), dim3(p.n_items), dim3(256), 0, s, p);
     return hipGetLastError();
   }
-  // Large grids: the 8-wavefront kernel (two wavefronts per SIMD). Small
-  // grids, which would leave CUs idle at 256 query rows per workgroup (a
-  // ring round of 4096 queries x 8 heads gives 128): the pipelined kernel.
-  // Both give the same bits.
+  // The 8-wavefront kernel (two wavefronts per SIMD, 256 rows per
+  // workgroup) unless its grid would leave CUs idle where the pipelined
+  // kernel's would not (a ring round of 4096 queries x 8 heads: 128
+  // workgroups of 256 rows against 256 of 128). Both give the same bits.
   const int64_t w8_items = (int64_t)p.B * p.H * ((p.Sq + kW8BM - 1) / kW8BM);
-  if (w8_items >= kW8MinItems) {
+  const int64_t sp_items = (int64_t)p.B * p.H * ((p.Sq + kSpBM - 1) / kSpBM);
+  if (prefer_two_waves(w8_items, sp_items, p.n_cu)) {
     p.n_qblk = (p.Sq + kW8BM - 1) / kW8BM;
     p.n_items = (int32_t)w8_items;
     hipLaunchKernelGGL(attn_fwd_bf16_w8_kernel, dim3(p.n_items), dim3(kW8Waves * 64), 0, s, p);

@@ -39,6 +39,7 @@ struct AttnParams {
   // nonzero: merge into the (O, LSE) already in o / lse (one ring round
   // folded into a running result) instead of overwriting them
   int32_t accumulate;
+  int32_t n_cu;       // compute units of the device (0: assume 256)
 };
 
 enum class DType : int { F32 = 0, BF16 = 1 };
@@ -92,7 +93,21 @@ struct BwdParams {
   float scale;        // score multiplier
   float scale_log2;   // scale * log2(e)
   int32_t n_qt;       // ceil(Sq / kBwdQT)
+  int32_t n_cu;       // compute units of the device (0: assume 256)
 };
+
+// Whether a kernel running two wavefronts per SIMD on workgroups of 2R
+// rows (items_big of them) should run rather than one running one
+// wavefront per SIMD on workgroups of R rows (items_small), judged by the
+// rounds each needs over the CUs: a workgroup of the former takes about
+// 5/3 as long as one of the latter (it does twice the work at about 1.2
+// times the rate), so it wins unless its last round leaves many CUs idle.
+inline bool prefer_two_waves(int64_t items_big, int64_t items_small, int n_cu) {
+  const int64_t cus = n_cu > 0 ? n_cu : 256;
+  const int64_t r_big = (items_big + cus - 1) / cus;
+  const int64_t r_small = (items_small + cus - 1) / cus;
+  return 5 * r_big <= 3 * r_small;
+}
 
 // Enqueues the three backward kernels (row statistics, dK/dV, dQ).
 hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t s);

@@ -199,9 +199,10 @@ def test_run_to_run_bit_identical(L):
 
 def test_workgroup_size_does_not_change_bits(L):
     """All 8 heads (512 workgroups of 256 rows: the eight-wavefront kernel)
-    vs a {1, 7} chunking and head 0 alone (grids of 128 and 896 rows-of-128
-    workgroups: the pipelined kernel): neither the kernel, the grid size nor
-    the chunking may change a bit."""
+    vs head 0 alone (128 workgroups of 128 rows: the pipelined kernel) and a
+    {1, 7} chunking (its 1-head chunk on the pipelined kernel, its 7-head
+    chunk on the eight-wavefront one): neither the kernel, the grid size
+    nor the chunking may change a bit."""
     G.announce("workgroup-size invariance")
     t = G.torch()
     S, H = 16384, 8
