@@ -168,18 +168,19 @@ def test_bwd_head_independence(L):
         assert t.equal(x[:, :, 1:3], y)
 
 
-@pytest.mark.parametrize("Skv", [1, 65, 129, 517])
-def test_bwd_large_grid_dq(L, Skv):
+@pytest.mark.parametrize("B,Skv", [(1, 1), (1, 65), (1, 129), (1, 517), (2, 300)])
+def test_bwd_large_grid_dq(L, B, Skv):
     """H=32, Sq=4133 (last 256-query block holds 37 rows): 544 workgroups
-    of 256 queries, so dQ runs on the two-wavefronts-per-SIMD kernel, over
-    1, 2, 3 and 9 key tiles (each load-ahead case, ragged last tiles).
-    Heads 0 and 31 against the oracle; every head bit-identical to calls on
-    4 heads at a time (68 workgroups: the pipelined dQ kernel)."""
+    of 256 queries per batch entry, so dQ runs on the two-wavefronts-per-
+    SIMD kernel, over 1, 2, 3, 5 and 9 key tiles (each load-ahead case,
+    ragged last tiles), and with B=2. Heads 0 and 31 against the oracle;
+    every head bit-identical to calls on 4 / B heads at a time (68
+    workgroups: the pipelined dQ kernel)."""
     t = G.torch()
-    B, Sq, H = 1, 4133, 32
-    G.announce(f"bwd large-grid dQ Skv={Skv}")
-    q, k, v = I.make_custom((B, Sq, H, 128), (B, Skv, H, 128), "bf16", seed=71 + Skv)
-    do = I.make_custom_dout((B, Sq, H, 128), "bf16", seed=71 + Skv)
+    Sq, H = 4133, 32
+    G.announce(f"bwd large-grid dQ B={B} Skv={Skv}")
+    q, k, v = I.make_custom((B, Sq, H, 128), (B, Skv, H, 128), "bf16", seed=71 + Skv + B)
+    do = I.make_custom_dout((B, Sq, H, 128), "bf16", seed=71 + Skv + B)
     full = [G.to_gpu(x, "bf16") for x in (q, k, v, do)]
     got = _grads(L, *full)
     heads = [0, 31]
@@ -187,8 +188,9 @@ def test_bwd_large_grid_dq(L, Skv):
                                    heads=heads)
     G.check_grads("bwd large grid", [x[:, :, heads] for x in _np(got)],
                   [r[:, :, heads] for r in ref])
-    for h0 in range(0, H, 4):
-        part = [x[:, :, h0:h0 + 4].contiguous() for x in full]
+    w = 4 // B   # heads per call: few enough workgroups for the pipelined kernel
+    for h0 in range(0, H, w):
+        part = [x[:, :, h0:h0 + w].contiguous() for x in full]
         sub = _grads(L, *part)
         for x, y in zip(got, sub):
-            assert t.equal(x[:, :, h0:h0 + 4], y), f"heads {h0}..{h0 + 3}"
+            assert t.equal(x[:, :, h0:h0 + w], y), f"heads {h0}..{h0 + w - 1}"
