@@ -33,17 +33,18 @@
 //    chosen, the workgroup size, the grid order, the number of heads or the
 //    strides.
 // Three bf16 kernels, two wavefronts per SIMD where the grid allows:
-//  * dense, large grids: eight wavefronts per workgroup (256 query rows),
-//    one workgroup per CU, each wavefront a plain loop over the key tiles;
-//    the SIMD overlaps one wavefront's softmax with the other's MFMAs;
+//  * dense: eight wavefronts per workgroup (256 query rows), one workgroup
+//    per CU, each wavefront a plain loop over the key tiles; the SIMD
+//    overlaps one wavefront's softmax with the other's MFMAs;
 //  * block-sparse: the same plain loop with four wavefronts (one 128-row
 //    mask row) and two workgroups per CU;
-//  * dense grids too small to fill the chip at 256 rows per workgroup (a
-//    ring round): four wavefronts, one per SIMD, each software-pipelining
-//    its key loop (matrix work of one tile interleaved with the softmax
-//    work of its neighbour).
+//  * dense grids that 256-row workgroups would leave partly idle where
+//    128-row ones would not (a ring round): four wavefronts, one per SIMD,
+//    each software-pipelining its key loop (matrix work of one tile
+//    interleaved with the softmax work of its neighbour).
 // fp32 inputs use v_mfma_f32_32x32x2_f32 with the same structure and P kept
-// in fp32.
+// in fp32. Every kernel writes a row through store_row, which can also fold
+// the row into a running (O, LSE) instead of overwriting it.
 #include "attn_common.hpp"
 
 #include <cstring>
