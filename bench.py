@@ -43,11 +43,20 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments, whitespace runs collapsed (a change to
+    comments alone leaves the kernel, and so this hash, as it was)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
