@@ -490,6 +490,11 @@ constexpr int kW4Slots = 2;
 template <int WAVES, int SLOTS, bool SPARSE>
 __device__ __forceinline__ void plain_attention(const AttnParams& p) {
   constexpr int BM = WAVES * kQW;
+  // LDS fragments read ahead of their MFMA. Scheduling barriers keep the
+  // reads where they are written: left to itself, the compiler sinks each
+  // read next to its MFMA (fewest registers), which exposes the LDS latency
+  // of every fragment.
+  constexpr int PF = 6;
   constexpr int LPW = (kTileBytes / 1024) / WAVES;   // 1-KiB loads per wavefront per tensor
   constexpr int DIST = SLOTS - 1;                      // tiles loaded ahead
   static_assert(LPW * WAVES * 1024 == kTileBytes, "tile/threads mismatch");
@@ -587,12 +592,14 @@ __device__ __forceinline__ void plain_attention(const AttnParams& p) {
     st[0] = f32x16{};
     st[1] = f32x16{};
     bf16x8 kf[16];
-    kf[0] = kread(slot, 0);
-    kf[1] = kread(slot, 1);
+#pragma unroll
+    for (int i = 0; i < PF; ++i) kf[i] = kread(slot, i);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if (i + 2 < 16) kf[i + 2] = kread(slot, i + 2);
       st[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i >> 1], st[i & 1], 0, 0, 0);
+      if (i + PF < 16) kf[i + PF] = kread(slot, i + PF);
+      __builtin_amdgcn_sched_barrier(0);
     }
     const int key0 = key0_of(t);
     if (key0 + kBN > p.Skv) {
@@ -643,13 +650,15 @@ __device__ __forceinline__ void plain_attention(const AttnParams& p) {
       }
     }
     bf16x8 vf[16];
-    vf[0] = vread(slot, 0);
-    vf[1] = vread(slot, 1);
+#pragma unroll
+    for (int i = 0; i < PF; ++i) vf[i] = vread(slot, i);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if (i + 2 < 16) vf[i + 2] = vread(slot, i + 2);
       const int db = i & 3, jj = (i >> 2) & 1, kb = i >> 3;
       acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[kb][jj], acc[db], 0, 0, 0);
+      if (i + PF < 16) vf[i + PF] = vread(slot, i + PF);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   // after step t: tile t+1 landed for every wavefront, slot of tile t free
