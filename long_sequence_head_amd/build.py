@@ -25,6 +25,7 @@ SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip", "aux_kernels.hip",
 # allocator otherwise shuttles them through AGPRs. The dK/dV kernel
 # (attn_bwd.hip) needs AGPRs for its 128 accumulators and keeps the default.
 FILE_FLAGS = {"attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+              "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
               "attn_bwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = "gfx950"
 

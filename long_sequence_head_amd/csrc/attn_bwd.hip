@@ -27,8 +27,9 @@
 // The dK/dV kernel runs one wavefront per SIMD, keeps three LDS slots per
 // streamed tensor and meets at one barrier per 64-row tile; the work of a
 // wavefront is software-pipelined over 32-row units. Its 128 accumulators
-// and K/V registers leave no room for a second wavefront per SIMD. The dQ
-// pass lives in attn_bwd_dq.hip, compiled with its MFMA results in VGPRs:
+// (in AGPRs) and K/V registers leave no room for a second wavefront per
+// SIMD. The dQ pass lives in attn_bwd_dq.hip, also compiled with its MFMA
+// results in VGPRs:
 // on large grids it runs eight wavefronts per workgroup, two per SIMD, each
 // in the plain order; on small grids a pipelined 4-wavefront kernel like
 // the dK/dV one.
@@ -68,6 +69,22 @@ __global__ __launch_bounds__(256) void attn_bwd_rows_kernel(BwdParams p) {
     a[0] = i < p.Sq ? p.lse[b * p.lse_sb + h * p.lse_sh + i] * kLog2e : __builtin_inff();
     a[kBwdQT] = acc;
   }
+}
+
+// dV^T / dK^T += A B with the accumulator held in AGPRs. This file is
+// compiled with MFMA results in VGPRs, so that S and dP (which the
+// elementwise step reads) need no copies out of AGPRs; the 128 accumulator
+// registers, which only MFMAs touch inside the loop, are pinned to AGPRs by
+// this asm instead. The compiler's hazard checks do not see into the asm:
+// within the loop an accumulator is reused 8 MFMAs later and its A and B
+// operands were written long before, so no wait states are needed there;
+// mfma_drain() covers the VALU writes before the first MFMA and the reads
+// after the last one.
+__device__ __forceinline__ void mfma_acc_agpr(f32x16& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_drain() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
 // --------------------------------------------------------------------- dK, dV
@@ -183,6 +200,7 @@ __global__ __launch_bounds__(kBwdWaves * 64, 1) void attn_bwd_dkdv_kernel(BwdPar
     acc_dv[db] = f32x16{};
     acc_dk[db] = f32x16{};
   }
+  mfma_drain();
   f32x16 sS, sD;            // S and dP of the unit in flight:
                             // register r <-> query 32 qb + 8 (r / 4) + 4 hh + r % 4
   bf16x8 pp[2][2], pds[2][2];   // P and dS of two consecutive units, as B operands
@@ -233,9 +251,9 @@ __global__ __launch_bounds__(kBwdWaves * 64, 1) void attn_bwd_dkdv_kernel(BwdPar
         if (m + 2 < 16) f[m + 2] = frag(m + 2);
         const int jj = m >> 3, db = (m >> 1) & 3;
         if (m & 1)
-          acc_dk[db] = mfma16(f[m], pds[sb][jj], acc_dk[db]);
+          mfma_acc_agpr(acc_dk[db], f[m], pds[sb][jj]);
         else
-          acc_dv[db] = mfma16(f[m], pp[sb][jj], acc_dv[db]);
+          mfma_acc_agpr(acc_dv[db], f[m], pp[sb][jj]);
       }
       if (DO_E) {
         const int r = m, g = r >> 2, e = r & 3;
@@ -304,6 +322,7 @@ __global__ __launch_bounds__(kBwdWaves * 64, 1) void attn_bwd_dkdv_kernel(BwdPar
   }
 
   // ---- epilogue: lane = key, registers = head_dim 32 db + 8 g4 + 4 hh + 0..3
+  mfma_drain();
   if (!k_ok) return;
   float* dvp = p.dv + b * p.dv_sb + h * p.dv_sh + (int64_t)kj * p.dv_ss;
   float* dkp = p.dk + b * p.dk_sb + h * p.dk_sh + (int64_t)kj * p.dk_ss;
