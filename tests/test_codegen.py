@@ -9,6 +9,8 @@ hipcc cross-compiles without a GPU).
   spill in the key loop costs far more than it saves. A few spilled words
   outside the loops (values that live across the key loop but are not used
   in it) cost nothing measurable and are allowed, up to 64 bytes.
+* The dK/dV kernel's query loop copies nothing out of AGPRs: only its
+  accumulators live there, pinned by an asm MFMA.
 * Inside the loops, a wait on the vector-memory counter may only come right
   before a barrier. The tile loads into LDS are inline asm the compiler does
   not count, so a wait it inserts for a load it does see (say, of Q) would
@@ -119,3 +121,21 @@ def test_vmcnt_waits_in_loops_only_before_barriers(asm):
                                 ("s_branch", "s_cbranch", "s_mov_b64", "s_andn2_b64", "s_and_b64",
                                  "s_waitcnt"))]
                     assert rest and rest[0] == "s_barrier", (name, l, code[i + 1:i + 4])
+
+
+def test_dkdv_loop_reads_no_agprs(asm):
+    """The dK/dV kernel keeps its accumulators in AGPRs through an asm MFMA
+    and every other MFMA result in VGPRs, so its query loop must not copy
+    values out of AGPRs (each `v_accvgpr_read` there is a VALU instruction
+    the elementwise step would pay for)."""
+    bodies = {n: l for n, l in _attention_bodies(asm).items() if "dkdv" in n}
+    if not bodies:
+        pytest.skip("no dK/dV kernel in this file")
+    for name, lines in bodies.items():
+        loops = _loops(lines)
+        assert loops, (name, "no loop found")
+        for a, b in loops:
+            bad = [l.strip() for l in lines[a:b + 1] if "v_accvgpr_read" in l]
+            assert not bad, (name, len(bad), bad[:3])
+            mfma = [l for l in lines[a:b + 1] if "v_mfma_f32_32x32x16_bf16" in l]
+            assert any(re.search(r"v_mfma\S*\s+a\[", l) for l in mfma), (name, "no AGPR accumulator")
