@@ -17,8 +17,9 @@
  * Conventions shared by every entry point.
  *  - Pointers named q, k, v, o, lse, src, dst, o_parts, lse_parts,
  *    block_mask, dout, dq, dk, dv and workspace are DEVICE pointers owned
- *    by the caller. The library allocates no device memory and keeps no
- *    per-call state.
+ *    by the caller. No call allocates device memory and none keeps
+ *    per-call state; the one static device array of the library (see
+ *    lsh_attn_fwd_blocksparse_noalloc) is part of its loaded code.
  *  - Streams are hipStream_t values passed as void*; NULL is the null
  *    stream. Every function only enqueues work and returns; results are
  *    ready when the stream(s) reach that point.
@@ -233,6 +234,26 @@ lsh_status lsh_attn_fwd_blocksparse(const lsh_attn_args* args,
 
 /* Workspace bytes of lsh_attn_fwd_blocksparse. 0 on bad args. */
 size_t lsh_attn_fwd_blocksparse_workspace(const lsh_attn_args* args);
+
+/*
+ * lsh_attn_fwd_blocksparse without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving
+ * loops, harnesses that forbid allocation). Same arguments, kernels and
+ * results (bit-identical) as lsh_attn_fwd_blocksparse; the launch schedule
+ * goes to a static device array of LSH_NOALLOC_SCRATCH_BYTES instead of a
+ * workspace. The call allocates nothing. Each GPU holds its own array from
+ * the library's load until the process ends; the schedule kernels overwrite
+ * every byte they use, so nothing needs clearing between calls, and the
+ * schedule of the last call stays readable there only by the library.
+ * Calls that overlap on one GPU (two streams, or two threads) share the
+ * array and race: order them on one stream. Returns LSH_ERR_WORKSPACE,
+ * before any HIP call, when lsh_attn_fwd_blocksparse_workspace(args)
+ * exceeds LSH_NOALLOC_SCRATCH_BYTES.
+ */
+#define LSH_NOALLOC_SCRATCH_BYTES (16u << 20)
+lsh_status lsh_attn_fwd_blocksparse_noalloc(const lsh_attn_args* args,
+                                            const uint8_t* block_mask,
+                                            lsh_stream stream);
 
 /*
  * Arguments of one attention backward (bf16 only).

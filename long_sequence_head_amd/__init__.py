@@ -16,6 +16,8 @@ Functions:
   lse_merge           merge of per-block partial results
   head_permute        [B, S, H, D] -> [B, hc, S, D] copy of heads [h0, h0+hc)
   attn_fwd_blocksparse  attention restricted to a 128x128 block mask
+  attn_fwd_blocksparse_noalloc  the same without a workspace (its schedule
+                      goes to the library's static device array)
   attn_bwd            gradients dQ, dK, dV of the dense forward (bf16)
 
 Submodule balance: host-side load-balance diagnostics of the block-sparse
@@ -32,7 +34,7 @@ from ._lib import LshError, load  # noqa: F401
 
 __all__ = ["attn_fwd", "attn_fwd_chunked", "attn_partial", "attn_partial_accumulate",
            "lse_merge", "head_permute",
-           "attn_fwd_blocksparse", "attn_bwd", "bwd_workspace_bytes",
+           "attn_fwd_blocksparse", "attn_fwd_blocksparse_noalloc", "attn_bwd", "bwd_workspace_bytes",
            "chunked_workspace_bytes", "blocksparse_workspace_bytes",
            "LshError", "load", "MASK_BLOCK"]
 
@@ -192,10 +194,13 @@ def attn_fwd_chunked(q, k, v, head_chunks, scale=None, o=None, lse=None, workspa
     st = lib.lsh_attn_fwd_chunked(ctypes.byref(a), chunks, len(head_chunks), ctypes.c_void_p(aligned),
                                   avail, ctypes.c_void_p(sc.cuda_stream), ctypes.c_void_p(sp.cuda_stream))
     _lib.check("lsh_attn_fwd_chunked", st)
-    if sp is not sc:
-        # the caching allocator must not hand these out while the permute stream uses them
-        for t in (workspace, q, k, v):
-            t.record_stream(sp)
+    # The caching allocator must not hand these out again while another
+    # stream than the current one still uses them.
+    cur = torch.cuda.current_stream(q.device)
+    for s_ in {sp, sc}:
+        if s_ != cur:
+            for t in (workspace, q, k, v, o, lse):
+                t.record_stream(s_)
     return o, lse
 
 
@@ -277,6 +282,29 @@ def attn_fwd_blocksparse(q, k, v, block_mask, scale=None, o=None, lse=None, work
                                       ctypes.c_void_p(aligned), workspace.numel() - (aligned - base),
                                       _stream_ptr(stream))
     _lib.check("lsh_attn_fwd_blocksparse", st)
+    return o, lse
+
+
+def attn_fwd_blocksparse_noalloc(q, k, v, block_mask, scale=None, o=None, lse=None,
+                                 stream=None):
+    """attn_fwd_blocksparse without a workspace: the launch schedule goes to
+    the library's static device array (no allocation in the library; pass o
+    and lse to allocate nothing here either). Calls overlapping on one GPU
+    race on that array."""
+    lib = load()
+    torch = _torch()
+    o, lse = _outputs(q, o, lse)
+    a = _args(q, k, v, o, lse, scale)
+    B, Sq, H, _ = q.shape
+    Skv = k.shape[1]
+    want = (B, H, -(-Sq // MASK_BLOCK), -(-Skv // MASK_BLOCK))
+    if block_mask.dtype != torch.uint8 or tuple(block_mask.shape) != want or not block_mask.is_contiguous():
+        raise ValueError(f"block_mask must be contiguous uint8 {want}")
+    if not block_mask.is_cuda:
+        raise ValueError("block_mask must be a GPU tensor")
+    st = lib.lsh_attn_fwd_blocksparse_noalloc(ctypes.byref(a), ctypes.c_void_p(block_mask.data_ptr()),
+                                              _stream_ptr(stream))
+    _lib.check("lsh_attn_fwd_blocksparse_noalloc", st)
     return o, lse
 
 

@@ -59,6 +59,7 @@ SIGNATURES = {
     "lsh_head_permute": (ctypes.c_int, [c_vp, c_vp, c_i32, c_i64, c_i64, c_i64, c_i64, c_i32, c_i32, c_vp]),
     "lsh_attn_fwd_blocksparse": (ctypes.c_int, [_ARGS_P, c_vp, c_vp, ctypes.c_size_t, c_vp]),
     "lsh_attn_fwd_blocksparse_workspace": (ctypes.c_size_t, [_ARGS_P]),
+    "lsh_attn_fwd_blocksparse_noalloc": (ctypes.c_int, [_ARGS_P, c_vp, c_vp]),
     "lsh_attn_bwd": (ctypes.c_int, [_BWD_P, c_vp, ctypes.c_size_t, c_vp]),
     "lsh_attn_bwd_workspace": (ctypes.c_size_t, [_BWD_P]),
 }

@@ -239,6 +239,72 @@ lsh_status hip_status(hipError_t e, const char* fn) {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Checks of a block-sparse call shared by both entry points (no HIP call).
+lsh_status validate_blocksparse(const lsh_attn_args* args, const uint8_t* block_mask,
+                                const char* fn) {
+  lsh_status st = validate_attn(args, false, fn);
+  if (st != LSH_OK) return st;
+  if (!block_mask) return fail(LSH_ERR_INVALID, "%s: block_mask is NULL", fn);
+  const int64_t n_mkb = (args->Skv + LSH_MASK_BLOCK - 1) / LSH_MASK_BLOCK;
+  if (n_mkb > 32768) return fail(LSH_ERR_UNSUPPORTED, "%s: Skv above 2^22 is not supported", fn);
+  return LSH_OK;
+}
+
+// Enqueues the schedule kernels and the block-sparse kernel (arguments checked).
+lsh_status blocksparse_launch(const lsh_attn_args* args, const uint8_t* block_mask,
+                              void* workspace, hipStream_t s, const char* fn) {
+  const int64_t n_mqb = (args->Sq + LSH_MASK_BLOCK - 1) / LSH_MASK_BLOCK;
+  const int64_t n_mkb = (args->Skv + LSH_MASK_BLOCK - 1) / LSH_MASK_BLOCK;
+  lsh::AttnParams p = make_params(args);
+  p.mask = block_mask;
+  p.n_mqb = (int32_t)n_mqb;
+  p.n_mkb = (int32_t)n_mkb;
+  const int32_t n_items = (int32_t)(args->B * args->H * n_mqb);
+  // workspace: int32 counts[n_items] | int32 order[n_items] | int64 totals[B * H]
+  const size_t region = round_up((size_t)n_items * sizeof(int32_t), 256);
+  int32_t* counts = static_cast<int32_t*>(workspace);
+  int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + region);
+  long long* totals = reinterpret_cast<long long*>(static_cast<char*>(workspace) + 2 * region);
+  hipError_t e = lsh::launch_sparse_schedule(block_mask, n_items, p.n_mkb, p.n_mqb, counts, totals,
+                                             order, s);
+  if (e != hipSuccess) return hip_status(e, fn);
+  p.order = order;
+  return hip_status(lsh::launch_attn_sparse(p, static_cast<lsh::DType>(args->dtype), s), fn);
+}
+
+
+// Static scratch of the allocation-free block-sparse entry point: the
+// launch schedule lives here instead of in a caller workspace. Each device
+// holds its own copy for the life of the process. In host code `scratch`
+// only names the symbol; its device address comes from hipGetSymbolAddress,
+// taken once per device with that device current.
+constexpr size_t kScratchBytes = LSH_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (checked by the caller).
+lsh_status scratch_ptr(void** out, const char* fn) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return fail(LSH_ERR_NO_DEVICE, "%s: no current device", fn);
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(LSH_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LSH_OK;
+}
+
 // Events of the chunk pipeline, created once per device and reused under a
 // lock (a stream wait captures the event state at the time of the call).
 constexpr int kMaxChunks = 64;
@@ -454,35 +520,35 @@ size_t lsh_attn_fwd_blocksparse_workspace(const lsh_attn_args* args) {
 lsh_status lsh_attn_fwd_blocksparse(const lsh_attn_args* args, const uint8_t* block_mask,
                                     void* workspace, size_t workspace_bytes, lsh_stream stream) {
   const char* fn = "lsh_attn_fwd_blocksparse";
-  lsh_status st = validate_attn(args, false, fn);
+  lsh_status st = validate_blocksparse(args, block_mask, fn);
   if (st != LSH_OK) return st;
-  if (!block_mask) return fail(LSH_ERR_INVALID, "%s: block_mask is NULL", fn);
-  const int64_t n_mqb = (args->Sq + LSH_MASK_BLOCK - 1) / LSH_MASK_BLOCK;
-  const int64_t n_mkb = (args->Skv + LSH_MASK_BLOCK - 1) / LSH_MASK_BLOCK;
-  if (n_mkb > 32768) return fail(LSH_ERR_UNSUPPORTED, "%s: Skv above 2^22 is not supported", fn);
   const size_t need = lsh_attn_fwd_blocksparse_workspace(args);
   if (!workspace || workspace_bytes < need)
     return fail(LSH_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(LSH_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
   if ((st = device_check_impl()) != LSH_OK) return st;
-  lsh::AttnParams p = make_params(args);
-  p.mask = block_mask;
-  p.n_mqb = (int32_t)n_mqb;
-  p.n_mkb = (int32_t)n_mkb;
-  const int32_t n_items = (int32_t)(args->B * args->H * n_mqb);
-  // workspace: int32 counts[n_items] | int32 order[n_items] | int64 totals[B * H]
-  const size_t region = round_up((size_t)n_items * sizeof(int32_t), 256);
-  int32_t* counts = static_cast<int32_t*>(workspace);
-  int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + region);
-  long long* totals = reinterpret_cast<long long*>(static_cast<char*>(workspace) + 2 * region);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = lsh::launch_sparse_schedule(block_mask, n_items, p.n_mkb, p.n_mqb, counts, totals,
-                                             order, s);
-  if (e != hipSuccess) return hip_status(e, fn);
-  p.order = order;
-  return hip_status(lsh::launch_attn_sparse(p, static_cast<lsh::DType>(args->dtype), s), fn);
+  return blocksparse_launch(args, block_mask, workspace, static_cast<hipStream_t>(stream), fn);
 }
+
+lsh_status lsh_attn_fwd_blocksparse_noalloc(const lsh_attn_args* args, const uint8_t* block_mask,
+                                            lsh_stream stream) {
+  const char* fn = "lsh_attn_fwd_blocksparse_noalloc";
+  lsh_status st = validate_blocksparse(args, block_mask, fn);
+  if (st != LSH_OK) return st;
+  const size_t need = lsh_attn_fwd_blocksparse_workspace(args);
+  if (need > kScratchBytes)
+    return fail(LSH_ERR_WORKSPACE,
+                "%s: the schedule needs %zu bytes, more than the %zu-byte static scratch; use "
+                "lsh_attn_fwd_blocksparse with a caller workspace",
+                fn, need, kScratchBytes);
+  if ((st = device_check_impl()) != LSH_OK) return st;
+  void* ws = nullptr;
+  if ((st = scratch_ptr(&ws, fn)) != LSH_OK) return st;
+  return blocksparse_launch(args, block_mask, ws, static_cast<hipStream_t>(stream), fn);
+}
+
+
 
 size_t lsh_attn_bwd_workspace(const lsh_attn_bwd_args* args) {
   if (validate_bwd(args, "lsh_attn_bwd_workspace") != LSH_OK) return 0;

@@ -197,6 +197,27 @@ def test_blocksparse_validation():
         assert lib.lsh_attn_fwd_blocksparse(ctypes.byref(a), m, m, need, None) == _lib.LSH_ERR_NO_DEVICE
 
 
+def test_blocksparse_noalloc_validation():
+    """The allocation-free entry point checks its arguments like the
+    workspace one and refuses, before any HIP call, a schedule larger than
+    its static array (16 MiB: 8 bytes per query block plus 8 per head)."""
+    lib = _lib_or_skip()
+    a = _valid_args(Sq=300, Skv=257, H=4)
+    m = 1 << 22
+    fn = lib.lsh_attn_fwd_blocksparse_noalloc
+    assert fn(ctypes.byref(a), None, None) == _lib.LSH_ERR_INVALID
+    assert fn(None, m, None) == _lib.LSH_ERR_INVALID
+    big = _valid_args(Sq=128 * 300, Skv=128, H=8192)
+    for f in ("q_stride", "k_stride", "v_stride", "o_stride"):
+        getattr(big, f)[:] = [0, 0, 0]
+    need = lib.lsh_attn_fwd_blocksparse_workspace(ctypes.byref(big))
+    assert need > (16 << 20)
+    assert fn(ctypes.byref(big), m, None) == _lib.LSH_ERR_WORKSPACE
+    assert b"static scratch" in lib.lsh_last_error()
+    if not _torch_cuda():
+        assert fn(ctypes.byref(a), m, None) == _lib.LSH_ERR_NO_DEVICE
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="build the HIP library"):
