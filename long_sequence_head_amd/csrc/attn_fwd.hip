@@ -109,33 +109,15 @@ __device__ __forceinline__ void store_row(const AttnParams& p, float* op, float*
   if (hh == 0) *lsep = mx + __logf(z);
 }
 
-// Builds, in LDS, the ascending list of kept key blocks of one mask row.
-// Returns the number of kept blocks (same value in every thread).
+// Copies the ascending list of kept key blocks of one mask row (left in
+// the workspace by the schedule kernels) into LDS. Returns their number.
 template <int NT>
-__device__ int build_kept_list(const uint8_t* mrow, int n_mkb, unsigned short* kept,
-                               int* wave_cnt) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  constexpr int W = NT / 64;
-  int total = 0;
-  for (int base = 0; base < n_mkb; base += NT) {
-    const int j = base + tid;
-    const bool flag = j < n_mkb && mrow[j] != 0;
-    const unsigned long long bal = __ballot(flag);
-    const int below = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) wave_cnt[wave] = __builtin_popcountll(bal);
-    __syncthreads();
-    int before = 0, sum = 0;
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const int c = wave_cnt[w];
-      before += (w < wave) ? c : 0;
-      sum += c;
-    }
-    if (flag) kept[total + before + below] = (unsigned short)j;
-    total += sum;
-    __syncthreads();
-  }
-  return total;
+__device__ int load_kept_list(const AttnParams& p, int item, unsigned short* kept) {
+  const int n_kept = p.counts[item];
+  const unsigned short* src = p.kept + (int64_t)item * p.n_mkb;
+  for (int j = threadIdx.x; j < n_kept; j += NT) kept[j] = src[j];
+  __syncthreads();
+  return n_kept;
 }
 
 // Start key of tile t: dense tiles are consecutive; sparse tiles are the two
@@ -149,366 +131,71 @@ __device__ __forceinline__ int tile_key0(int t, const unsigned short* kept) {
   }
 }
 
-// ------------------------------------ bf16, one wavefront per SIMD, pipelined
+// --------------------- bf16, 16x16x32 MFMA, pipelined 32-key units
 //
-// Four wavefronts of 32 query rows each, one per SIMD. Each wavefront runs a
-// software pipeline over the key tiles, so that its own instruction stream
-// keeps the matrix core and the VALU busy together:
-//   phase 1 of step t: S(t+1) = K(t+1) Q^T (16 MFMA), interleaved with the
-//       exp2 of the already-scaled S(t) into x(t) (fp32) and P(t) (bf16);
-//   phase 2 of step t: O^T += V(t)^T P(t)^T (16 MFMA), interleaved with the
-//       row sum of x(t), the row max of S(t+1), the lazy-rescale decision and
-//       the scaling s c - m c of S(t+1).
-// Every query's arithmetic (product order, exp2 arguments, summation order,
-// rescale points, bf16 rounding of P) depends on its own scores only, and is
-// the same as in the plain kernels below, so every kernel, grid and head
-// chunking gives the same bits.
+// A wavefront owns 32 query rows as two groups of 16 (qg = 0, 1). The key
+// loop works in units of 32 keys (half a 64-key tile). For unit u:
+//  * scores S_u^T = K_u Q^T on v_mfma_f32_16x16x32_bf16: four 16 x 16
+//    blocks (two 16-key groups kg x two query groups), each summed over four
+//    32-wide head_dim chunks. Lane l (t = l % 16, g = l / 16) holds keys
+//    16 kg + 4 g + i (i = 0..3) of query 16 qg + t, so each query's 32 keys
+//    lie in the four lanes t, t + 16, t + 32, t + 48;
+//  * softmax of the unit, lane by lane: x = exp2(s c - m c), l += x in key
+//    order (kg, then i), P = bf16(x). A lane's 8 values of query group qg
+//    are exactly the B operand (32 keys x 16 queries) of the next product,
+//    with the keys in the order the lanes hold them;
+//  * output O^T += V_u^T P_u^T: eight 16-wide head_dim groups x two query
+//    groups, one MFMA each. The V^T operand takes the same key order: two
+//    transposing LDS reads of 4 keys each per lane.
+// Each K fragment read from LDS feeds the two query groups, and so does each
+// V fragment. The 16x16x32 form keeps 4 accumulator registers per MFMA
+// instead of 16: for the same flops it moves less register data, which is
+// what sets the sustained clock of an MFMA-bound kernel on this GPU.
 //
-// K/V tiles go HBM -> LDS directly (buffer_load ... lds) into two slots per
-// tensor. Each slot is its own LDS variable and every access names its slot
-// at compile time (the step loop is unrolled by two), so the compiler can
-// tell the LDS reads of one slot from the loads in flight into the other;
-// the loads are issued from inline asm (lds_dma16), so control-flow joins do
-// not make the reads wait for them either. A step has two barriers: one after
-// phase 1 (all wavefronts are done with K(t+1)), one after phase 2 (done
-// with V(t)). Step t issues V(t+1) at its start, into the slot V(t-1) left,
-// and K(t+3) after its middle barrier, into the slot K(t+1) left; each load
-// has about one and a half steps to land, and a wavefront waits only for
-// the loads the next phase reads.
-
-constexpr int kSpWaves = 4;
-constexpr int kSpBM = kSpWaves * kQW;   // 128 query rows per workgroup
-
-__global__ __launch_bounds__(kSpWaves * 64, 1) void attn_fwd_bf16_sp_kernel(AttnParams p) {
-  constexpr int LPW = (kTileBytes / 1024) / kSpWaves;   // 1-KiB loads per wavefront per tensor
-  static_assert(LPW * kSpWaves * 1024 == kTileBytes, "tile/threads mismatch");
-
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_k0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_k1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_v0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_v1[kTileBytes];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hh = lane >> 5;
-
-  // workgroups walk the items XCD by XCD
-  const Item it = decode_item(xcd_remap(blockIdx.x, gridDim.x), p.n_qblk, p.H);
-  const int qi = it.qblk * kSpBM + wave * kQW + l32;
-  const bool q_ok = qi < p.Sq;
-  const __bf16* qp = static_cast<const __bf16*>(p.q) + it.b * p.q_sb + it.h * p.q_sh;
-  const __bf16* kp = static_cast<const __bf16*>(p.k) + it.b * p.k_sb + it.h * p.k_sh;
-  const __bf16* vp = static_cast<const __bf16*>(p.v) + it.b * p.v_sb + it.h * p.v_sh;
-
-  // 64-key tiles in order; only the last can be ragged
-  const int n_tiles = (p.Skv + kBN - 1) / kBN;
-  auto key0_of = [&](int t) __device__ -> int { return t * kBN; };
-
-  // Q fragments (B operand of S^T = K Q^T): lane holds Q[qi][16 s + 8 hh .. +7].
-  bf16x8 qf[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s)
-    qf[s] = q_ok ? *reinterpret_cast<const bf16x8*>(qp + (int64_t)qi * p.q_ss + 16 * s + 8 * hh)
-                 : bf16x8{};
-
-  // ---- tile loads: every wavefront issues LPW 1-KiB loads per tensor tile.
-  // Load j of this wavefront fills tile rows 4 (wave LPW + j) .. +3; lane l
-  // fills LDS chunk l%16 of its row, which holds the row's global chunk
-  // (l%16) ^ swizzle(row). A buffer resource over the head's rows makes
-  // loads past the last key return zeros.
-  const uint32_t k_rb = (uint32_t)(p.k_ss * 2), v_rb = (uint32_t)(p.v_ss * 2);
-  const int k_rec = (int)((uint32_t)(p.Skv - 1) * k_rb + kD * 2);
-  const int v_rec = (int)((uint32_t)(p.Skv - 1) * v_rb + kD * 2);
-  uint32_t koff[LPW], voff[LPW];
-#pragma unroll
-  for (int j = 0; j < LPW; ++j) {
-    const int r = 4 * (wave * LPW + j) + (lane >> 4);
-    const int pos = lane & 15;
-    koff[j] = (uint32_t)r * k_rb + ((uint32_t)swz_k(r, pos) << 4);
-    voff[j] = (uint32_t)r * v_rb + ((uint32_t)swz_v(r, pos) << 4);
-  }
-  auto kslot = [&](int slot) __device__ -> unsigned char* { return slot ? lds_k1 : lds_k0; };
-  auto vslot = [&](int slot) __device__ -> unsigned char* { return slot ? lds_v1 : lds_v0; };
-  // descriptors over the head's K and V rows (loads past the last key
-  // return zeros)
-  const i32x4 k_rsrc = make_rsrc(kp, k_rec), v_rsrc = make_rsrc(vp, v_rec);
-  auto issue_k = [&](int t) __device__ {
-    const uint32_t base = (uint32_t)key0_of(t) * k_rb;
-    const uint32_t dst = lds_addr(kslot(t & 1)) + wave * LPW * 1024;
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) lds_dma16(dst + j * 1024, koff[j] + base, k_rsrc);
-  };
-  auto issue_v = [&](int t) __device__ {
-    const uint32_t base = (uint32_t)key0_of(t) * v_rb;
-    const uint32_t dst = lds_addr(vslot(t & 1)) + wave * LPW * 1024;
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) lds_dma16(dst + j * 1024, voff[j] + base, v_rsrc);
-  };
-
-  // ---- LDS fragment offsets inside a tile (per lane, loop-invariant). K
-  // fragment i = 2 s + kb reads row kb*32 + l32, head_dim 16 s + 8 hh .. +7;
-  // V^T fragment i = (kb*2 + jj)*4 + db is a transposing read (tr_read).
-  uint32_t kofs[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) kofs[s] = (uint32_t)(l32 * 256 + (swz_k(l32, 2 * s + hh) << 4));
-  uint32_t vofs[2][4];
-  tr_offsets(lane, vofs);
-  auto kread = [&](int slot, int i) __device__ -> bf16x8 {
-    const LDS_AS unsigned char* b = (LDS_AS const unsigned char*)kslot(slot);
-    return *(LDS_AS const bf16x8*)(b + kofs[i >> 1] + (i & 1) * 8192);
-  };
-  auto vread = [&](int slot, int i) __device__ -> bf16x8 { return tr_read(vslot(slot), vofs, i); };
-
-  // ---- softmax state
-  const float c = p.scale_log2;
-  f32x16 acc[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
-  float m_run = kNegInf;   // running max of raw scores (both halves agree)
-  float mc = 0.0f;         // m_run * c, or 0 while m_run = -inf
-  float l_run = 0.0f;      // this half's partial sum of exp2(s c - m c)
-  f32x16 sa[2], sb[2];     // S of two consecutive tiles: st[kb][r]
-  bf16x8 pf[2][2];         // P(t): pf[kb][jj]
-
-  // Row max of the raw scores st -> lazy-rescale decision -> st becomes
-  // s c - m c. Split into 16 slices that phase 2 spreads over its 16 MFMAs:
-  // slices 0-7 take the max of scores 4k .. 4k+3, slice 8 decides, slices
-  // 9-15 scale five scores each.
-  float part_max = kNegInf, alpha = 1.0f;
-  bool any_need = false;
-  auto softmax_slice = [&](f32x16 (&st)[2], int k) __device__ {
-    if (k < 8) {
-#pragma unroll
-      for (int e = 4 * k; e < 4 * k + 4; ++e) part_max = fmaxf(part_max, st[e >> 4][e & 15]);
-    } else if (k == 8) {
-      const float mx = pair_max(part_max);
-      part_max = kNegInf;
-      const bool need = (mx - m_run) * c > kRescaleLog2;
-      const float m_new = need ? mx : m_run;
-      alpha = need ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.0f;
-      any_need = wave_any(need);
-      m_run = m_new;
-      mc = (m_run == kNegInf) ? 0.0f : m_run * c;
-    } else {
-      const int e0 = 5 * (k - 9), e1 = e0 + 5 < 32 ? e0 + 5 : 32;
-#pragma unroll
-      for (int e = e0; e < e1; ++e) {
-        float y = __builtin_fmaf(st[e >> 4][e & 15], c, -mc);
-        asm volatile("" : "+v"(y));   // computed here, not sunk into the next step
-        st[e >> 4][e & 15] = y;
-      }
-    }
-  };
-  auto mask_tile = [&](f32x16 (&st)[2], int key0) __device__ {
-    if (key0 + kBN > p.Skv) {
-      const int lim = p.Skv - key0 - 4 * hh;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int off = 8 * (r >> 2) + (r & 3);
-        if (off >= lim) st[0][r] = kNegInf;
-        if (off + 32 >= lim) st[1][r] = kNegInf;
-      }
-    }
-  };
-
-  // phase 1 of step t: S(t+1) -> sn (if DO_QK), interleaved with
-  // x(t) = exp2(sc) kept in sc and P(t) = bf16(x(t)) in pf
-  auto phase1 = [&](const bool DO_QK, int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) __device__ {
-    const int ks = (t + 1) & 1;
-    bf16x8 kf[16];
-    if (DO_QK) {
-      kf[0] = kread(ks, 0);
-      kf[1] = kread(ks, 1);
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (DO_QK) {
-        if (i + 2 < 16) kf[i + 2] = kread(ks, i + 2);
-        if (i < 2)
-          sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i >> 1], f32x16{}, 0, 0, 0);
-        else
-          sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i >> 1], sn[i & 1], 0, 0, 0);
-      }
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int e = 2 * i + q, kb = e >> 4, r = e & 15;
-        const float x = __builtin_amdgcn_exp2f(sc[kb][r]);
-        asm volatile("" ::"v"(x));   // computed here, next to this MFMA
-        sc[kb][r] = x;
-        pf[kb][r >> 3][r & 7] = (__bf16)x;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // phase 2 of step t: O^T += V(t)^T P(t)^T, interleaved with l += x(t) and
-  // (if HAS_NEXT) the softmax slices of S(t+1)
-  auto phase2 = [&](const bool HAS_NEXT, const bool MAYBE_RAGGED, int t, f32x16 (&sc)[2],
-                    f32x16 (&sn)[2]) __device__ {
-    if (HAS_NEXT && MAYBE_RAGGED) mask_tile(sn, key0_of(t + 1));
-    const int vs = t & 1;
-    bf16x8 vf[16];
-    vf[0] = vread(vs, 0);
-    vf[1] = vread(vs, 1);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i + 2 < 16) vf[i + 2] = vread(vs, i + 2);
-      const int db = i & 3, jj = (i >> 2) & 1, kb = i >> 3;
-      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[kb][jj], acc[db], 0, 0, 0);
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int e = 2 * i + q;
-        float l = l_run + sc[e >> 4][e & 15];
-        asm volatile("" : "+v"(l));   // summed here, in key order
-        l_run = l;
-      }
-      if (HAS_NEXT) softmax_slice(sn, i);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (HAS_NEXT) {
-      l_run *= alpha;
-      if (any_need) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) acc[db] *= alpha;
-      }
-    }
-  };
-
-  // waits until at most n (0, LPW or 2 LPW) of this wavefront's loads are
-  // still in flight
-  auto wait_le = [&](int n) __device__ {
-    if (n == 0) wait_vmcnt<0>();
-    else if (n == LPW) wait_vmcnt<LPW>();
-    else wait_vmcnt<2 * LPW>();
-  };
-
-  // A sparse row without kept blocks attends to no key: it skips straight
-  // to the epilogue, which writes O = 0 and LSE = -inf.
-  if (n_tiles > 0) {
-    // ---- prologue: K0, K1 and V0 in flight; S(0), its max, the rescale
-    // decision and its scaling once K0 landed; then K1 must have landed and
-    // K2 goes into K0's slot.
-    issue_k(0);
-    if (n_tiles > 1) issue_k(1);
-    issue_v(0);
-    wait_le(n_tiles > 1 ? 2 * LPW : LPW);
-    barrier_no_fence();
-    {
-      sa[0] = f32x16{};
-      sa[1] = f32x16{};
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        sa[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(0, i), qf[i >> 1], sa[i & 1], 0, 0, 0);
-      mask_tile(sa, key0_of(0));
-#pragma unroll
-      for (int k = 0; k < 16; ++k) softmax_slice(sa, k);
-      l_run *= alpha;   // l_run = 0: the product stays 0
-    }
-    wait_le(LPW);   // K1 (V0 may stay in flight)
-    barrier_no_fence();
-    if (n_tiles > 2) issue_k(2);
-
-    // one step: tile t's scaled scores in sc, S(t+1) into sn (if HAS_NEXT,
-    // i.e. t + 1 < n_tiles)
-    auto step = [&](const bool HAS_NEXT, const bool MAYBE_RAGGED, int t, f32x16 (&sc)[2],
-                    f32x16 (&sn)[2]) __device__ {
-      if (HAS_NEXT) issue_v(t + 1);
-      phase1(HAS_NEXT, t, sc, sn);
-      // V(t) next; in flight after it: K(t+2), V(t+1)
-      wait_le((t + 2 < n_tiles ? LPW : 0) + (HAS_NEXT ? LPW : 0));
-      barrier_no_fence();
-      if (t + 3 < n_tiles) issue_k(t + 3);
-      phase2(HAS_NEXT, MAYBE_RAGGED, t, sc, sn);
-      if (t + 2 < n_tiles) {
-        // K(t+2) next; in flight after it: V(t+1), K(t+3)
-        wait_le((HAS_NEXT ? LPW : 0) + (t + 3 < n_tiles ? LPW : 0));
-        barrier_no_fence();
-      }
-    };
-
-    // t is even at the top of the loop, so every slot index above is a
-    // compile-time constant. Tiles before the last one are never ragged: the
-    // loop runs steps whose next tile is at most n_tiles - 2.
-    int t = 0;
-    for (; t + 3 < n_tiles; t += 2) {
-      step(true, false, t, sa, sb);
-      step(true, false, t + 1, sb, sa);
-    }
-    const int rest = n_tiles - t;   // 1, 2 or 3
-    if (rest == 3) {
-      step(true, false, t, sa, sb);
-      step(true, true, t + 1, sb, sa);
-      step(false, false, t + 2, sa, sa);
-    } else if (rest == 2) {
-      step(true, true, t, sa, sb);
-      step(false, false, t + 1, sb, sb);
-    } else {
-      step(false, false, t, sa, sa);
-    }
-  }   // n_tiles > 0
-
-  // ---- epilogue: combine halves, normalise, write O and LSE
-  const float l_tot = pair_sum(l_run);
-  if (!q_ok) return;
-  store_row(p, p.o + it.b * p.o_sb + it.h * p.o_sh + (int64_t)qi * p.o_ss,
-            p.lse + it.b * p.lse_sb + it.h * p.lse_sh + qi, hh, l_tot, m_run, acc);
-}
-
-// ------------------------- bf16, two wavefronts per SIMD, plain key loop
+// Stage k of a wavefront issues the scores of unit k+1 and the output of
+// unit k-1 on the matrix cores, with the softmax of unit k spread over the
+// same 8 slots (two scores per slot). Tile step t is the two stages 2t+1
+// and 2t+2: they read K of tile t+1 and V of tile t only.
 //
-// Each wavefront (32 query rows) runs the plain step per 64-key tile: S = K
-// Q^T (16 MFMA), the online softmax of S (same arithmetic, in the same
-// order, as the pipelined kernel above, so both give the same bits), then
-// O^T += V^T P^T (16 MFMA). Instead of software-pipelining one wavefront,
-// two wavefronts on a SIMD fill each other's gaps: one runs its softmax on
-// the VALU while the other's MFMAs keep the matrix core busy.
-//  * Dense (attn_fwd_bf16_w8_kernel): eight wavefronts and 256 query rows
-//    per workgroup, one workgroup per CU. Every K/V tile serves 256 rows,
-//    half the LDS fill per query of a 128-row workgroup. Three LDS slots per
-//    tensor (96 KiB), tiles loaded two ahead: step t waits for tile t+1
-//    (tile t+2 may still be in flight), meets the other wavefronts at one
-//    barrier (after which slot t is free) and issues tile t+3 into it.
-//  * Block-sparse (attn_fwd_bf16_w4s_kernel): four wavefronts on one
-//    128-row mask row, streaming the 64-key halves of its kept blocks in
-//    ascending order (without a half wholly past the last key, so only the
-//    last tile can be ragged). Two slots per tensor (64 KiB), tiles loaded
-//    one ahead, so that two workgroups, each with its own mask row, share a
-//    CU. A row without kept blocks gets O = 0 and LSE = -inf.
-// Both fit 256 registers per wavefront, which is what lets two wavefronts
-// share a SIMD.
+// Lazy rescale per unit and query: the exponentials use the running max as
+// it stands; if a lane's 8 terms of the unit sum to at most 128 (and the max
+// is set) none exceeds 2^7, so no score has passed the max by more than 2^8
+// and the values stand. Otherwise the unit's row max (over the four lanes)
+// decides whether the max moves; if it does, O (after the stage's output
+// MFMAs, which still use the old max) and l are rescaled and the unit's
+// exponentials are redone. Every query's arithmetic depends on its own
+// scores only, in an order fixed per query, so every kernel built from this
+// template (any wavefront count, grid, head chunking, strides or block mask
+// that keeps the same keys) gives the same bits.
+//
+// K and V tiles have separate rings of S LDS slots each, filled by LDS DMA.
+// After tile step t the slots of K(t+1) and V(t) are free; K(t+1+S) and
+// V(t+S) go into them. O leaves through LDS so that each query row is
+// written as whole 128-byte lines.
 
-constexpr int kW8Waves = 8;
-constexpr int kW8BM = kW8Waves * kQW;   // 256 query rows per workgroup
-constexpr int kW8Slots = 3;             // LDS slots per tensor
-// Block-sparse: 4 wavefronts (one 128-row mask row), two workgroups per CU
-// (their LDS, 2 x 64 KiB plus the kept-block lists, fits in 160 KiB).
-constexpr int kW4Waves = 4;
-constexpr int kW4Slots = 2;
+// V rows are swizzled by 16-byte chunk as chunk ^ 2 (row % 8): the
+// transposing reads of one instruction (8 rows x 32 bytes per half
+// wavefront) then hit every LDS bank once.
+__device__ __forceinline__ int swz_v16(int row, int c) { return c ^ (2 * (row & 7)); }
 
-// The plain kernel body. WAVES wavefronts of 32 query rows; SLOTS LDS slots
-// per tensor, tiles loaded SLOTS-1 ahead.
-template <int WAVES, int SLOTS, bool SPARSE>
-__device__ __forceinline__ void plain_attention(const AttnParams& p) {
+template <int WAVES, int S, bool SPARSE>
+__device__ __forceinline__ void attention16(const AttnParams& p) {
   constexpr int BM = WAVES * kQW;
-  // LDS fragments read ahead of their MFMA. Scheduling barriers keep the
-  // reads where they are written: left to itself, the compiler sinks each
-  // read next to its MFMA (fewest registers), which exposes the LDS latency
-  // of every fragment.
-  constexpr int PF = 6;
-  constexpr int LPW = (kTileBytes / 1024) / WAVES;   // 1-KiB loads per wavefront per tensor
-  constexpr int DIST = SLOTS - 1;                      // tiles loaded ahead
+  constexpr int LPW = (kTileBytes / 1024) / WAVES;   // 1-KiB loads per wavefront per tile
+  constexpr int PF = 2;                                // fragment reads ahead, in slots
+  constexpr int kSlotBytes = kTileBytes;
   static_assert(LPW * WAVES * 1024 == kTileBytes, "tile/threads mismatch");
+  static_assert(S == 2 || S == 3, "2 or 3 slots per ring");
   static_assert(!SPARSE || BM == kMaskBlock, "a sparse workgroup covers one mask row");
-  static_assert(DIST == 1 || DIST == 2, "one or two tiles ahead");
+  static_assert(WAVES * 8192 <= 2 * S * kSlotBytes, "epilogue staging must fit the tile slots");
 
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_k[SLOTS][kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_v[SLOTS][kTileBytes];
-  extern __shared__ unsigned short kept_dyn[];   // sparse: kept key blocks of the mask row
-  __shared__ int wave_cnt[WAVES];
+  // K slots 0..S-1, then V slots 0..S-1
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_buf[2 * S * kSlotBytes];
+  extern __shared__ unsigned short kept_dyn[];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hh = lane >> 5;
+  const int t16 = lane & 15, g = lane >> 4;
   int item;
   if constexpr (SPARSE) {
     item = p.order ? p.order[blockIdx.x] : (int)blockIdx.x;
@@ -516,35 +203,39 @@ __device__ __forceinline__ void plain_attention(const AttnParams& p) {
     item = xcd_remap(blockIdx.x, gridDim.x);
   }
   const Item it = decode_item(item, p.n_qblk, p.H);
-  const int qi = it.qblk * BM + wave * kQW + l32;
-  const bool q_ok = qi < p.Sq;
+  const int q0 = it.qblk * BM + wave * kQW;   // first query row of the wavefront
   const __bf16* qp = static_cast<const __bf16*>(p.q) + it.b * p.q_sb + it.h * p.q_sh;
   const __bf16* kp = static_cast<const __bf16*>(p.k) + it.b * p.k_sb + it.h * p.k_sh;
   const __bf16* vp = static_cast<const __bf16*>(p.v) + it.b * p.v_sb + it.h * p.v_sh;
-  int n_tiles;
+  int n;   // key tiles
   if constexpr (SPARSE) {
-    const uint8_t* mrow = p.mask + (((int64_t)it.b * p.H + it.h) * p.n_mqb + it.qblk) * p.n_mkb;
-    const int n_kept = build_kept_list<WAVES * 64>(mrow, p.n_mkb, kept_dyn, wave_cnt);
-    n_tiles = 2 * n_kept;
-    if (n_kept > 0 && (int)kept_dyn[n_kept - 1] * kMaskBlock + kBN >= p.Skv) n_tiles -= 1;
+    const int n_kept = load_kept_list<WAVES * 64>(p, item, kept_dyn);
+    n = 2 * n_kept;
+    if (n_kept > 0 && (int)kept_dyn[n_kept - 1] * kMaskBlock + kBN >= p.Skv) n -= 1;
   } else {
-    n_tiles = (p.Skv + kBN - 1) / kBN;
+    n = (p.Skv + kBN - 1) / kBN;
   }
   auto key0_of = [&](int t) __device__ -> int { return tile_key0<SPARSE>(t, kept_dyn); };
 
-  // Q fragments (B operand of S^T = K Q^T): lane holds Q[qi][16 s + 8 hh .. +7].
-  bf16x8 qf[8];
+  // Q fragments (B operand of S^T = K Q^T): qf[qg][dc] holds
+  // Q[q0 + 16 qg + t][32 dc + 8 g .. +7].
+  bf16x8 qf[2][4];
 #pragma unroll
-  for (int s = 0; s < 8; ++s)
-    qf[s] = q_ok ? *reinterpret_cast<const bf16x8*>(qp + (int64_t)qi * p.q_ss + 16 * s + 8 * hh)
-                 : bf16x8{};
-  // Q has landed before any tile load is issued. The compiler does not see
-  // the tile loads (inline asm), so a Q load it still thought in flight
-  // would make it wait on the vector-memory counter inside the key loop,
-  // which would also wait for the tiles prefetched ahead.
+  for (int qg = 0; qg < 2; ++qg) {
+    const int qi = q0 + 16 * qg + t16;
+#pragma unroll
+    for (int dc = 0; dc < 4; ++dc)
+      qf[qg][dc] = qi < p.Sq
+                       ? *reinterpret_cast<const bf16x8*>(qp + (int64_t)qi * p.q_ss + 32 * dc + 8 * g)
+                       : bf16x8{};
+  }
+  // Q lands before any tile load is issued (the tile loads are invisible to
+  // the compiler, which would otherwise wait for them with the Q loads).
   wait_vmcnt<0>();
 
-  // tile loads and LDS fragment reads: as in the pipelined kernel
+  // ---- tile loads: load j of this wavefront fills tile rows 4 (wave LPW +
+  // j) .. +3; lane l fills LDS chunk l % 16 of its row with the row's global
+  // chunk (l % 16) ^ swizzle(row).
   const uint32_t k_rb = (uint32_t)(p.k_ss * 2), v_rb = (uint32_t)(p.v_ss * 2);
   const int k_rec = (int)((uint32_t)(p.Skv - 1) * k_rb + kD * 2);
   const int v_rec = (int)((uint32_t)(p.Skv - 1) * v_rb + kD * 2);
@@ -554,194 +245,431 @@ __device__ __forceinline__ void plain_attention(const AttnParams& p) {
     const int r = 4 * (wave * LPW + j) + (lane >> 4);
     const int pos = lane & 15;
     koff[j] = (uint32_t)r * k_rb + ((uint32_t)swz_k(r, pos) << 4);
-    voff[j] = (uint32_t)r * v_rb + ((uint32_t)swz_v(r, pos) << 4);
+    voff[j] = (uint32_t)r * v_rb + ((uint32_t)swz_v16(r, pos) << 4);
   }
-  auto kslot = [&](int slot) __device__ -> unsigned char* { return lds_k[slot]; };
-  auto vslot = [&](int slot) __device__ -> unsigned char* { return lds_v[slot]; };
   const i32x4 k_rsrc = make_rsrc(kp, k_rec), v_rsrc = make_rsrc(vp, v_rec);
-  auto issue = [&](int t, int slot) __device__ {
-    const uint32_t key0 = (uint32_t)key0_of(t);
-    const uint32_t bk = key0 * k_rb, bv = key0 * v_rb;
-    const uint32_t dk = lds_addr(kslot(slot)) + wave * LPW * 1024;
-    const uint32_t dv = lds_addr(vslot(slot)) + wave * LPW * 1024;
+  const uint32_t lds0 = lds_addr(lds_buf);
+  auto issue_k = [&](int t) __device__ {
+    const uint32_t base = (uint32_t)key0_of(t) * k_rb;
+    const uint32_t dst = lds0 + (t % S) * kSlotBytes + wave * LPW * 1024;
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) lds_dma16(dk + j * 1024, koff[j] + bk, k_rsrc);
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) lds_dma16(dv + j * 1024, voff[j] + bv, v_rsrc);
+    for (int j = 0; j < LPW; ++j) lds_dma16(dst + j * 1024, koff[j] + base, k_rsrc);
   };
-  uint32_t kofs[8];
+  auto issue_v = [&](int t) __device__ {
+    const uint32_t base = (uint32_t)key0_of(t) * v_rb;
+    const uint32_t dst = lds0 + (S + t % S) * kSlotBytes + wave * LPW * 1024;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) kofs[s] = (uint32_t)(l32 * 256 + (swz_k(l32, 2 * s + hh) << 4));
-  uint32_t vofs[2][4];
-  tr_offsets(lane, vofs);
-  auto kread = [&](int slot, int i) __device__ -> bf16x8 {
-    const LDS_AS unsigned char* b = (LDS_AS const unsigned char*)kslot(slot);
-    return *(LDS_AS const bf16x8*)(b + kofs[i >> 1] + (i & 1) * 8192);
+    for (int j = 0; j < LPW; ++j) lds_dma16(dst + j * 1024, voff[j] + base, v_rsrc);
   };
-  auto vread = [&](int slot, int i) __device__ -> bf16x8 { return tr_read(vslot(slot), vofs, i); };
+  // loads of batch b (issued after tile step b): K(b+1+S) and V(b+S)
+  auto batch_loads = [&](int b) __device__ -> int {
+    return LPW * ((b + 1 + S < n ? 1 : 0) + (b + S < n ? 1 : 0));
+  };
+  auto issue_batch = [&](int b) __device__ {
+    if (b + 1 + S < n) issue_k(b + 1 + S);
+    if (b + S < n) issue_v(b + S);
+  };
+  // waits until at most `left` of this wavefront's tile loads are in flight
+  auto wait_left = [&](int left) __device__ {
+    switch (left) {
+      case 0: wait_vmcnt<0>(); break;
+      case LPW: wait_vmcnt<LPW>(); break;
+      case 2 * LPW: wait_vmcnt<2 * LPW>(); break;
+      case 3 * LPW: wait_vmcnt<3 * LPW>(); break;
+      case 4 * LPW: wait_vmcnt<4 * LPW>(); break;
+      default: wait_vmcnt<0>(); break;
+    }
+  };
+  // loads that may stay in flight at the end of tile step t (t >= -1): the
+  // batches after the one that brought K(t+2) and V(t+1)
+  auto left_after = [&](int t) __device__ -> int {
+    int cnt = 0;
+#pragma unroll
+    for (int b = 2 - S; b <= -1; ++b) cnt += batch_loads(t + b);
+    return cnt;
+  };
+
+  // ---- LDS fragment offsets (per lane, loop-invariant).
+  // K fragment (16 keys x 32 head_dim: A operand) of key group kg and
+  // head_dim chunk dc in unit half uh: row 32 uh + 16 kg + t, global chunk
+  // 4 dc + g, stored at chunk (4 dc + g) ^ t.
+  uint32_t kofs[4];
+#pragma unroll
+  for (int dc = 0; dc < 4; ++dc) kofs[dc] = (uint32_t)(t16 * 256 + (((4 * dc + g) ^ t16) << 4));
+  // V^T fragment (16 head_dim x 32 keys: A operand) of head_dim group dg:
+  // lane (g, t) receives column 16 dg + t of unit rows 4 g .. 4 g + 3, then
+  // of rows 16 + 4 g .. +3; for that it points at row 4 g + t / 4 (+16),
+  // columns 16 dg + 4 (t % 4) .. +3.
+  const int vr = 4 * g + (t16 >> 2);
+  const uint32_t vbase = (uint32_t)(vr * 256 + 16 * ((t16 >> 1) & 1) + 8 * (t16 & 1));
+  uint32_t vofs[8];
+#pragma unroll
+  for (int dg = 0; dg < 8; ++dg) vofs[dg] = vbase + 32u * (uint32_t)(dg ^ (vr & 7));
+  auto kread = [&](int slot, int uh, int kg, int dc) __device__ -> bf16x8 {
+    const LDS_AS unsigned char* b = (LDS_AS const unsigned char*)lds_buf + slot * kSlotBytes;
+    return *(LDS_AS const bf16x8*)(b + kofs[dc] + uh * 8192 + kg * 4096);
+  };
+  auto vread = [&](int slot, int uh, int dg) __device__ -> bf16x8 {
+    const LDS_AS unsigned char* b =
+        (LDS_AS const unsigned char*)lds_buf + (S + slot) * kSlotBytes + uh * 8192 + vofs[dg];
+    const s16x4 w0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)b);
+    const s16x4 w1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(b + 4096));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
 
   const float c = p.scale_log2;
-  f32x16 acc[4];
+  f32x4 acc[8][2];   // O^T[dg][qg]
 #pragma unroll
-  for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
-  float m_run = kNegInf, mc = 0.0f, l_run = 0.0f;
+  for (int dg = 0; dg < 8; ++dg) acc[dg][0] = acc[dg][1] = f32x4{};
+  float m_run[2] = {kNegInf, kNegInf}, mc[2] = {0.0f, 0.0f}, l_run[2] = {0.0f, 0.0f};
+  f32x4 su[2][2][2];   // scores of two consecutive units (by parity): su[parity][kg][qg]
+  bf16x8 pu[2][2];     // P of two consecutive units (by parity): pu[parity][qg]
 
-  // one key tile in slot `slot`
-  auto step = [&](int slot, int t) __device__ {
-    f32x16 st[2];
-    st[0] = f32x16{};
-    st[1] = f32x16{};
-    bf16x8 kf[16];
+  auto mask_unit = [&](f32x4 (&st)[2][2], int kb0) __device__ {
+    if (kb0 + 32 > p.Skv) {
+      const int lim = p.Skv - kb0 - 4 * g;
 #pragma unroll
-    for (int i = 0; i < PF; ++i) kf[i] = kread(slot, i);
-    __builtin_amdgcn_sched_barrier(0);
+      for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      st[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i >> 1], st[i & 1], 0, 0, 0);
-      if (i + PF < 16) kf[i + PF] = kread(slot, i + PF);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < 4; ++i)
+          if (16 * kg + i >= lim) st[kg][0][i] = st[kg][1][i] = kNegInf;
     }
-    const int key0 = key0_of(t);
-    if (key0 + kBN > p.Skv) {
-      const int lim = p.Skv - key0 - 4 * hh;
+  };
+  // scores i = 2 h and 2 h + 1 of the lane's 8 for query group qg and key
+  // group kg: x = exp2(s c - m c), l += x in key order, P = bf16(x)
+  auto score2 = [&](const f32x4 (&st)[2][2], bf16x8 (&pc)[2], int qg, int kg, int h) __device__ {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int off = 8 * (r >> 2) + (r & 3);
-        if (off >= lim) st[0][r] = kNegInf;
-        if (off + 32 >= lim) st[1][r] = kNegInf;
+    for (int q = 0; q < 2; ++q) {
+      const int i = 2 * h + q;
+      const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kg][qg][i], c, -mc[qg]));
+      l_run[qg] = l_run[qg] + x;
+      pc[qg][4 * kg + i] = (__bf16)x;
+    }
+  };
+  auto max4 = [&](float x) __device__ -> float {
+    x = fmaxf(x, __shfl_xor(x, 16));
+    return fmaxf(x, __shfl_xor(x, 32));
+  };
+  // end of a unit's softmax: the lazy-rescale check (see above)
+  auto unit_check = [&](const f32x4 (&st)[2][2], bf16x8 (&pc)[2], const float (&l0)[2]) __device__ {
+    const bool sure0 = m_run[0] != kNegInf && l_run[0] - l0[0] <= kSureSum;
+    const bool sure1 = m_run[1] != kNegInf && l_run[1] - l0[1] <= kSureSum;
+    if (wave_any(!(sure0 && sure1))) {
+      bool need[2];
+      float mx[2];
+#pragma unroll
+      for (int qg = 0; qg < 2; ++qg) {
+        float pm = kNegInf;
+#pragma unroll
+        for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pm = fmaxf(pm, st[kg][qg][i]);
+        mx[qg] = max4(pm);
+        need[qg] = (mx[qg] - m_run[qg]) * c > kRescaleLog2;
       }
-    }
-    // x = exp2(s c - m c), l += x in key order, P = bf16(x), first with the
-    // running max as it stands. That is the lazy rescale's answer unless a
-    // score exceeds the max by more than 2^8 in probability, which needs a
-    // tile sum of x above 256; a sum within 128 (and a max already set)
-    // rules it out without the row max. Otherwise the row max is taken and
-    // the rescale decided as usual; if it fires, the exponentials are redone
-    // with the new max. Either way the values are those of the plain order.
-    const float l0 = l_run;
-    bf16x8 pf[2][2];
+      if (wave_any(need[0] || need[1])) {
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(st[e >> 4][e & 15], c, -mc));
-      l_run = l_run + x;
-      pf[e >> 4][(e & 15) >> 3][e & 7] = (__bf16)x;
-    }
-    const bool sure = m_run != kNegInf && l_run - l0 <= kSureSum;
-    if (wave_any(!sure)) {
-      float part_max = kNegInf;
+        for (int qg = 0; qg < 2; ++qg) {
+          const float m_new = need[qg] ? mx[qg] : m_run[qg];
+          const float alpha = need[qg] ? __builtin_amdgcn_exp2f((m_run[qg] - m_new) * c) : 1.0f;
+          m_run[qg] = m_new;
+          mc[qg] = (m_new == kNegInf) ? 0.0f : m_new * c;
+          l_run[qg] = l0[qg] * alpha;
 #pragma unroll
-      for (int e = 0; e < 32; ++e) part_max = fmaxf(part_max, st[e >> 4][e & 15]);
-      const float mx = pair_max(part_max);
-      const bool need = (mx - m_run) * c > kRescaleLog2;
-      if (wave_any(need)) {
-        const float m_new = need ? mx : m_run;
-        const float alpha = need ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.0f;
-        m_run = m_new;
-        mc = (m_run == kNegInf) ? 0.0f : m_run * c;
-        l_run = l0 * alpha;
+          for (int dg = 0; dg < 8; ++dg) acc[dg][qg] *= alpha;
 #pragma unroll
-        for (int db = 0; db < 4; ++db) acc[db] *= alpha;
-#pragma unroll
-        for (int e = 0; e < 32; ++e) {
-          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(st[e >> 4][e & 15], c, -mc));
-          l_run = l_run + x;
-          pf[e >> 4][(e & 15) >> 3][e & 7] = (__bf16)x;
+          for (int kg = 0; kg < 2; ++kg) {
+            score2(st, pc, qg, kg, 0);
+            score2(st, pc, qg, kg, 1);
+          }
         }
       }
     }
-    bf16x8 vf[16];
+  };
+
+  // Slot j (0..15) of a tile step: stage j / 8, slot i = j % 8 of it. It
+  // issues the QK MFMAs of K fragment (kg = i / 4, dc = i % 4) of unit half
+  // j / 8 into both query groups, the PV MFMAs of V fragment dg = i of unit
+  // half j / 8 from both query groups' P, and two softmax scores (qg = i / 4,
+  // kg = (i / 2) % 2, i % 2) of the unit being exponentiated. Fragments are
+  // read PF slots ahead, across the two stages of the step.
+  auto kfrag = [&](int ks, int j) __device__ -> bf16x8 {
+    return kread(ks, j >> 3, (j >> 2) & 1, j & 3);
+  };
+  auto vfrag = [&](int vs, int j) __device__ -> bf16x8 { return vread(vs, j >> 3, j & 7); };
+
+  // Tile step t: stage A = slots 0..7 (QK unit 2t+2, PV unit 2t, softmax
+  // unit 2t+1), stage B = slots 8..15 (QK unit 2t+3, PV unit 2t+1, softmax
+  // unit 2t+2). Units of parity 0 live in su[0] / pu[0], parity 1 in su[1] /
+  // pu[1]. j0 = t % S (a compile-time constant at every call). Stage B's
+  // lazy-rescale check runs at the start of the next tile step (it has to
+  // precede only the output MFMAs of unit 2t+2 and the softmax of unit
+  // 2t+3), beside that step's first fragment reads; `check_b` returns the
+  // sums it needs.
+  auto tile_step = [&](int t, int j0, bool has_next, bool ragged, bool pending,
+                       const float (&lb)[2], float (&lb_next)[2]) __device__ {
+    const int ks = (j0 + 1) % S, vs = j0 % S;
+    bf16x8 kf[16], vf[16];
 #pragma unroll
-    for (int i = 0; i < PF; ++i) vf[i] = vread(slot, i);
+    for (int j = 0; j < PF; ++j) {
+      if (has_next) kf[j] = kfrag(ks, j);
+      vf[j] = vfrag(vs, j);
+    }
+    // the previous stage B's check: unit 2t (parity 0)
+    if (pending) unit_check(su[0], pu[0], lb);
+    if (ragged) mask_unit(su[1], key0_of(t) + 32);
+    float la[2] = {l_run[0], l_run[1]};
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int db = i & 3, jj = (i >> 2) & 1, kb = i >> 3;
-      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[kb][jj], acc[db], 0, 0, 0);
-      if (i + PF < 16) vf[i + PF] = vread(slot, i + PF);
+    for (int j = 0; j < 16; ++j) {
+      const int i = j & 7, kg = i >> 2, dc = i & 3;
+      const int par = j >> 3;   // 0: stage A, 1: stage B
+      if (j == 8) {
+        // end of stage A: softmax unit 2t+1 is complete
+        unit_check(su[1], pu[1], la);
+        if (has_next && ragged) mask_unit(su[0], key0_of(t + 1));
+        la[0] = l_run[0];
+        la[1] = l_run[1];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      f32x4 (&sn)[2][2] = su[par];          // QK target: unit 2t+2+par
+      const bf16x8 (&pp)[2] = pu[par];      // PV source: unit 2t+par
+      if (has_next) {
+#pragma unroll
+        for (int qg = 0; qg < 2; ++qg)
+          sn[kg][qg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j], qf[qg][dc],
+                                                               dc == 0 ? f32x4{} : sn[kg][qg], 0, 0, 0);
+      }
+#pragma unroll
+      for (int qg = 0; qg < 2; ++qg)
+        acc[i][qg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[j], pp[qg], acc[i][qg], 0, 0, 0);
+      if (j + PF < 16) {
+        if (has_next) kf[j + PF] = kfrag(ks, j + PF);
+        vf[j + PF] = vfrag(vs, j + PF);
+      }
+      // softmax: stage A exponentiates unit 2t+1 (parity 1), stage B unit
+      // 2t+2 (parity 0, only if it exists)
+      if (par == 0) score2(su[1], pu[1], i >> 2, (i >> 1) & 1, i & 1);
+      else if (has_next) score2(su[0], pu[0], i >> 2, (i >> 1) & 1, i & 1);
+      if (has_next) {
+        // the slot's order: MFMA, LDS read, 3 VALU, MFMA, LDS read, MFMA,
+        // LDS read, 3 VALU, MFMA, 2 VALU. Left to itself the compiler groups
+        // the four MFMAs, and with the two wavefronts of a SIMD in step the
+        // matrix core then waits out both VALU groups.
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
+    lb_next[0] = la[0];
+    lb_next[1] = la[1];
   };
-  // after step t: tile t+1 landed for every wavefront, slot of tile t free
-  auto advance = [&](int slot, int t) __device__ {
-    if (t + 1 < n_tiles) {
-      if constexpr (DIST == 2) {
-        if (t + 2 < n_tiles) wait_vmcnt<2 * LPW>();   // tile t+2 may stay in flight
-        else wait_vmcnt<0>();
-      } else {
-        wait_vmcnt<0>();
+  // end of tile step t: K(t+2) and V(t+1) landed everywhere, then the freed
+  // slots are refilled
+  auto step_end = [&](int t, bool steady) __device__ {
+    if (steady) wait_vmcnt<(S - 2) * 2 * LPW>();
+    else wait_left(left_after(t));
+    barrier_no_fence();
+    issue_batch(t);
+  };
+
+  if (n > 0) {
+    // prologue: K(0), then the batches before the first tile step
+    issue_k(0);
+#pragma unroll
+    for (int b = -S; b <= -2; ++b) issue_batch(b);
+    {
+      int c0 = 0;
+#pragma unroll
+      for (int b = -S; b <= -2; ++b) c0 += batch_loads(b);
+      wait_left(c0);
+    }
+    barrier_no_fence();
+    // Unit 0's scores, then unit 1's scores beside unit 0's softmax (K
+    // tile 0; no output yet).
+    float lb[2] = {0.0f, 0.0f};
+    {
+      bf16x8 kf[16];
+#pragma unroll
+      for (int j = 0; j < PF; ++j) kf[j] = kfrag(0, j);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int i = j & 7, kg = i >> 2, dc = i & 3, par = j >> 3;
+        if (j == 8) {
+          mask_unit(su[0], key0_of(0));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int qg = 0; qg < 2; ++qg)
+          su[par][kg][qg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              kf[j], qf[qg][dc], dc == 0 ? f32x4{} : su[par][kg][qg], 0, 0, 0);
+        if (j + PF < 16) kf[j + PF] = kfrag(0, j + PF);
+        if (par == 1) score2(su[0], pu[0], i >> 2, (i >> 1) & 1, i & 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      barrier_no_fence();
-      if (t + DIST + 1 < n_tiles) issue(t + DIST + 1, slot);
     }
-  };
+    step_end(-1, false);
 
-  // prologue: the first DIST + 1 tiles, then wait for tile 0
-  if (n_tiles > 0) issue(0, 0);
-  if constexpr (DIST == 2) {
-    if (n_tiles > 2) {
-      issue(1, 1);
-      issue(2, 2);
-      wait_vmcnt<4 * LPW>();
-    } else if (n_tiles > 1) {
-      issue(1, 1);
-      wait_vmcnt<2 * LPW>();
-    } else {
-      wait_vmcnt<0>();
-    }
-  } else {
-    if (n_tiles > 1) {
-      issue(1, 1);
-      wait_vmcnt<2 * LPW>();
-    } else {
-      wait_vmcnt<0>();
-    }
-  }
-  barrier_no_fence();
-  // t is a multiple of SLOTS at the top of the loop, so every slot index is
-  // a compile-time constant
-  int t = 0;
-  for (; t + SLOTS <= n_tiles; t += SLOTS) {
+    // Steady tile steps: not the last two tiles (no ragged unit, a next
+    // tile) and every batch of the rings full; t stays a multiple of S at
+    // the loop head so that every slot index is a compile-time constant.
+    int t = 0;
+    for (; t + S <= n - S - 1; t += S) {
 #pragma unroll
-    for (int j = 0; j < SLOTS; ++j) {
-      step(j, t + j);
-      advance(j, t + j);
+      for (int j = 0; j < S; ++j) {
+        float lb2[2];
+        tile_step(t + j, j, true, false, true, lb, lb2);
+        lb[0] = lb2[0];
+        lb[1] = lb2[1];
+        step_end(t + j, true);
+      }
     }
-  }
+    // the remaining r = n - t (1 .. 2S) tile steps: r - 1 with a next tile,
+    // then the last one; slot indices stay compile-time constants
+    const int r = n - t;
 #pragma unroll
-  for (int j = 0; j < SLOTS - 1; ++j) {
-    if (t < n_tiles) {
-      step(j, t);
-      advance(j, t);
-      ++t;
+    for (int j = 0; j < 2 * S - 1; ++j) {
+      if (j + 1 < r) {
+        float lb2[2];
+        tile_step(t + j, j % S, true, true, true, lb, lb2);
+        lb[0] = lb2[0];
+        lb[1] = lb2[1];
+        step_end(t + j, false);
+      }
+    }
+    float lb2[2];
+    switch ((r - 1) % S) {
+      case 0: tile_step(n - 1, 0, false, true, true, lb, lb2); break;
+      case 1: tile_step(n - 1, 1 % S, false, true, true, lb, lb2); break;
+      default: tile_step(n - 1, 2 % S, false, true, true, lb, lb2); break;
     }
   }
 
-  // ---- epilogue: combine halves, normalise, write O and LSE. The row's
-  // addresses are derived again here (from a copy of the thread id the
-  // compiler cannot match with the first), so that they do not occupy
-  // registers through the key loop.
-  const float l_tot = pair_sum(l_run);
+  // ---- epilogue. Row sums over the four lanes of a query (the same bits
+  // in all four), then O leaves through LDS: each wavefront stages 16 rows
+  // x 128 floats of its O per query group (chunk c of row t stored at chunk
+  // c ^ t), with the row's 1/l and LSE beside them, and writes whole rows.
+  float l_tot[2], lse_new[2], inv_l[2];
+#pragma unroll
+  for (int qg = 0; qg < 2; ++qg) {
+    const float a2 = l_run[qg] + __shfl_xor(l_run[qg], 16);
+    l_tot[qg] = a2 + __shfl_xor(a2, 32);
+    const bool empty = !(l_tot[qg] > 0.0f);
+    inv_l[qg] = empty ? 0.0f : 1.0f / l_tot[qg];
+    lse_new[qg] = empty ? kNegInf : m_run[qg] * p.scale + __logf(l_tot[qg]);
+  }
+  __syncthreads();   // every wavefront is done with the tile slots
+  unsigned char* stg = lds_buf + wave * 8192;
+  float* rowinfo = reinterpret_cast<float*>(lds_buf + WAVES * 8192) + wave * 32;
   int tid2 = (int)threadIdx.x;
   asm volatile("" : "+v"(tid2));
-  int item2;
-  if constexpr (SPARSE) {
-    item2 = p.order ? p.order[blockIdx.x] : (int)blockIdx.x;
-  } else {
-    item2 = xcd_remap(blockIdx.x, gridDim.x);
+  const int lane2 = tid2 & 63;
+#pragma unroll
+  for (int qg = 0; qg < 2; ++qg) {
+#pragma unroll
+    for (int dg = 0; dg < 8; ++dg) {
+      const int ch = 4 * dg + g;   // 16-byte chunk of the row
+      *reinterpret_cast<f32x4*>(stg + t16 * 512 + ((ch ^ t16) << 4)) = acc[dg][qg];
+    }
+    if (g == 0) {
+      rowinfo[2 * t16] = inv_l[qg];
+      rowinfo[2 * t16 + 1] = lse_new[qg];
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wavefront's LDS writes done
+    __builtin_amdgcn_wave_barrier();
+    const int qrow0 = q0 + 16 * qg;
+    float* obase = p.o + it.b * p.o_sb + it.h * p.o_sh;
+    float* lbase = p.lse + it.b * p.lse_sb + it.h * p.lse_sh;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int row = 2 * k + (lane2 >> 5), ch = lane2 & 31;
+      const int qi = qrow0 + row;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(stg + row * 512 + ((ch ^ row) << 4));
+      const float il = rowinfo[2 * row], ln = rowinfo[2 * row + 1];
+      if (qi < p.Sq) {
+        float* op = obase + (int64_t)qi * p.o_ss + 4 * ch;
+        if (!p.accumulate) {
+          f32x4 o4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o4[i] = a[i] * il;
+          *reinterpret_cast<f32x4*>(op) = o4;
+        } else {
+          // merge with the row's (O, LSE) so far, as two parts of a key
+          // partition: M = max(LSE_old, LSE_new), w = exp(LSE - M),
+          // Z = w_old + w_new, O = (w_old O_old + w_new O_new) / Z; a row
+          // whose two LSE are both -inf is left as it is
+          const float lo = lbase[qi];
+          const float mx = fmaxf(lo, ln);
+          if (mx != kNegInf) {
+            const float w_old = __expf(lo - mx), w_new = __expf(ln - mx);
+            const float z = w_old + w_new;
+            const float a_old = w_old / z, a_new = w_new / z * il;
+            const f32x4 old = *reinterpret_cast<const f32x4*>(op);
+            f32x4 o4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o4[i] = __builtin_fmaf(a[i], a_new, old[i] * a_old);
+            *reinterpret_cast<f32x4*>(op) = o4;
+          }
+        }
+      }
+    }
+    // LSE: lanes 0..15 write the group's 16 rows (all lanes of a row read
+    // the old LSE above before any lane writes it)
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    if (lane2 < 16) {
+      const int qi = qrow0 + lane2;
+      if (qi < p.Sq) {
+        const float ln = rowinfo[2 * lane2 + 1];
+        if (!p.accumulate) {
+          lbase[qi] = ln;
+        } else {
+          const float lo = lbase[qi];
+          const float mx = fmaxf(lo, ln);
+          if (mx != kNegInf) {
+            const float z = __expf(lo - mx) + __expf(ln - mx);
+            lbase[qi] = mx + __logf(z);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
   }
-  const Item it2 = decode_item(item2, p.n_qblk, p.H);
-  const int qi2 = it2.qblk * BM + (tid2 >> 6) * kQW + (tid2 & 31);
-  if (qi2 >= p.Sq) return;
-  store_row(p, p.o + it2.b * p.o_sb + it2.h * p.o_sh + (int64_t)qi2 * p.o_ss,
-            p.lse + it2.b * p.lse_sb + it2.h * p.lse_sh + qi2, hh, l_tot, m_run, acc);
 }
 
-__global__ __launch_bounds__(kW8Waves * 64, 1) void attn_fwd_bf16_w8_kernel(AttnParams p) {
-  plain_attention<kW8Waves, kW8Slots, false>(p);
+// The three bf16 kernels, one template:
+//  * dense, large grids: 8 wavefronts (256 query rows), one workgroup per
+//    CU, two wavefronts per SIMD, three slots per ring (96 KiB);
+//  * dense grids that 256-row workgroups would leave partly idle where
+//    128-row ones would not (a ring round of 4096 queries x 8 heads): 4
+//    wavefronts (128 rows), one wavefront per SIMD;
+//  * block-sparse: 4 wavefronts on one 128-row mask row, two workgroups per
+//    CU (two wavefronts per SIMD, each with its own mask row), two slots per
+//    ring (64 KiB each).
+constexpr int kP8Waves = 8;
+constexpr int kP8BM = kP8Waves * kQW;
+constexpr int kP4Waves = 4;
+constexpr int kP4BM = kP4Waves * kQW;
+
+__global__ __launch_bounds__(kP8Waves * 64, 1) void attn_fwd_bf16_p8_kernel(AttnParams p) {
+  attention16<kP8Waves, 3, false>(p);
 }
 
-__global__ __launch_bounds__(kW4Waves * 64, 2) void attn_fwd_bf16_w4s_kernel(AttnParams p) {
-  plain_attention<kW4Waves, kW4Slots, true>(p);
+__global__ __launch_bounds__(kP4Waves * 64, 1) void attn_fwd_bf16_p4_kernel(AttnParams p) {
+  attention16<kP4Waves, 3, false>(p);
+}
+
+__global__ __launch_bounds__(kP4Waves * 64, 2) void attn_fwd_bf16_s4_kernel(AttnParams p) {
+  attention16<kP4Waves, 2, true>(p);
 }
 
 // ------------------------------------------------------------------ f32 path
@@ -780,8 +708,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_f32_kernel(AttnParams p) 
   int n_tiles;
   const unsigned short* kept = kept_dyn;
   if constexpr (SPARSE) {
-    const uint8_t* mrow = p.mask + (((int64_t)it.b * p.H + it.h) * p.n_mqb + it.qblk) * p.n_mkb;
-    n_tiles = 2 * build_kept_list<NT>(mrow, p.n_mkb, kept_dyn, wave_cnt);
+    n_tiles = 2 * load_kept_list<NT>(p, item, kept_dyn);
   } else {
     n_tiles = (p.Skv + kBN - 1) / kBN;
   }
@@ -908,20 +835,20 @@ hipError_t launch_attn_dense(const AttnParams& p0, DType dt, hipStream_t s) {
     return hipGetLastError();
   }
   // The 8-wavefront kernel (two wavefronts per SIMD, 256 rows per
-  // workgroup) unless its grid would leave CUs idle where the pipelined
+  // workgroup) unless its grid would leave CUs idle where the 4-wavefront
   // kernel's would not (a ring round of 4096 queries x 8 heads: 128
   // workgroups of 256 rows against 256 of 128). Both give the same bits.
-  const int64_t w8_items = (int64_t)p.B * p.H * ((p.Sq + kW8BM - 1) / kW8BM);
-  const int64_t sp_items = (int64_t)p.B * p.H * ((p.Sq + kSpBM - 1) / kSpBM);
-  if (prefer_two_waves(w8_items, sp_items, p.n_cu)) {
-    p.n_qblk = (p.Sq + kW8BM - 1) / kW8BM;
-    p.n_items = (int32_t)w8_items;
-    hipLaunchKernelGGL(attn_fwd_bf16_w8_kernel, dim3(p.n_items), dim3(kW8Waves * 64), 0, s, p);
+  const int64_t p8_items = (int64_t)p.B * p.H * ((p.Sq + kP8BM - 1) / kP8BM);
+  const int64_t p4_items = (int64_t)p.B * p.H * ((p.Sq + kP4BM - 1) / kP4BM);
+  if (prefer_two_waves(p8_items, p4_items, p.n_cu)) {
+    p.n_qblk = (p.Sq + kP8BM - 1) / kP8BM;
+    p.n_items = (int32_t)p8_items;
+    hipLaunchKernelGGL(attn_fwd_bf16_p8_kernel, dim3(p.n_items), dim3(kP8Waves * 64), 0, s, p);
     return hipGetLastError();
   }
-  p.n_qblk = (p.Sq + kSpBM - 1) / kSpBM;
-  p.n_items = p.B * p.H * p.n_qblk;
-  hipLaunchKernelGGL(attn_fwd_bf16_sp_kernel, dim3(p.n_items), dim3(kSpWaves * 64), 0, s, p);
+  p.n_qblk = (p.Sq + kP4BM - 1) / kP4BM;
+  p.n_items = (int32_t)p4_items;
+  hipLaunchKernelGGL(attn_fwd_bf16_p4_kernel, dim3(p.n_items), dim3(kP4Waves * 64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -933,7 +860,7 @@ hipError_t launch_attn_sparse(const AttnParams& p0, DType dt, hipStream_t s) {
   if (dt == DType::F32)
     hipLaunchKernelGGL((attn_fwd_f32_kernel<4, true>), dim3(p.n_items), dim3(256), dyn, s, p);
   else
-    hipLaunchKernelGGL(attn_fwd_bf16_w4s_kernel, dim3(p.n_items), dim3(kW4Waves * 64), dyn, s, p);
+    hipLaunchKernelGGL(attn_fwd_bf16_s4_kernel, dim3(p.n_items), dim3(kP4Waves * 64), dyn, s, p);
   return hipGetLastError();
 }
 

@@ -124,17 +124,27 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(
 // processing time first): the hardware dispatcher then fills CUs greedily
 // and the light items pack the tail.
 
-// counts[item] = number of kept key blocks in the item's mask row.
+// counts[item] = number of kept key blocks in the item's mask row, and
+// kept[item][0 .. counts[item]) = those blocks' indices, ascending (one
+// wavefront per row: a ballot per 64 blocks, each kept block's slot is the
+// number of kept blocks before it).
 __global__ __launch_bounds__(256) void sparse_count_kernel(const uint8_t* __restrict__ mask,
                                                            int n_items, int n_mkb,
-                                                           int* __restrict__ counts) {
+                                                           int* __restrict__ counts,
+                                                           unsigned short* __restrict__ kept) {
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (item >= n_items) return;
   const uint8_t* row = mask + (int64_t)item * n_mkb;
+  unsigned short* krow = kept + (int64_t)item * n_mkb;
   int cnt = 0;
-  for (int j = lane; j < n_mkb; j += 64) cnt += row[j] != 0;
-  for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
+  for (int base = 0; base < n_mkb; base += 64) {
+    const int j = base + lane;
+    const bool flag = j < n_mkb && row[j] != 0;
+    const unsigned long long bal = __ballot(flag);
+    if (flag) krow[cnt + __builtin_popcountll(bal & ((1ull << lane) - 1ull))] = (unsigned short)j;
+    cnt += __builtin_popcountll(bal);
+  }
   if (lane == 0) counts[item] = cnt;
 }
 
@@ -230,9 +240,9 @@ hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, int32_
 
 hipError_t launch_sparse_schedule(const uint8_t* mask, int32_t n_items, int32_t n_mkb, int32_t per,
                                   int32_t* counts, long long* totals, int32_t* order,
-                                  hipStream_t s) {
+                                  unsigned short* kept, hipStream_t s) {
   hipLaunchKernelGGL(sparse_count_kernel, dim3((n_items + 3) / 4), dim3(256), 0, s, mask, n_items,
-                     n_mkb, counts);
+                     n_mkb, counts, kept);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_groups = n_items / per;

@@ -189,7 +189,10 @@ def test_blocksparse_validation():
     lib = _lib_or_skip()
     a = _valid_args(Sq=300, Skv=257, H=4)
     need = lib.lsh_attn_fwd_blocksparse_workspace(ctypes.byref(a))
-    assert need == 2 * ((4 * 3 * 4 + 255) // 256 * 256) + (4 * 8 + 255) // 256 * 256
+    # counts and order (int32 per item), totals (int64 per head), kept lists
+    # (uint16 per item and key block), each rounded up to 256 bytes
+    assert need == 2 * ((4 * 3 * 4 + 255) // 256 * 256) + (4 * 8 + 255) // 256 * 256 + \
+        (4 * 3 * 3 * 2 + 255) // 256 * 256
     m = 1 << 22
     assert lib.lsh_attn_fwd_blocksparse(ctypes.byref(a), None, m, need, None) == _lib.LSH_ERR_INVALID
     assert lib.lsh_attn_fwd_blocksparse(ctypes.byref(a), m, m, need - 1, None) == _lib.LSH_ERR_WORKSPACE
@@ -200,7 +203,8 @@ def test_blocksparse_validation():
 def test_blocksparse_noalloc_validation():
     """The allocation-free entry point checks its arguments like the
     workspace one and refuses, before any HIP call, a schedule larger than
-    its static array (16 MiB: 8 bytes per query block plus 8 per head)."""
+    its static array (16 MiB: 8 bytes per query block, 2 per query and key
+    block, 8 per head)."""
     lib = _lib_or_skip()
     a = _valid_args(Sq=300, Skv=257, H=4)
     m = 1 << 22

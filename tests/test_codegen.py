@@ -11,10 +11,12 @@ hipcc cross-compiles without a GPU).
   in it) cost nothing measurable and are allowed, up to 64 bytes.
 * The dK/dV kernel's query loop copies nothing out of AGPRs: only its
   accumulators live there, pinned by an asm MFMA.
-* Inside the loops, a wait on the vector-memory counter may only come right
-  before a barrier. The tile loads into LDS are inline asm the compiler does
-  not count, so a wait it inserts for a load it does see (say, of Q) would
-  also wait for the tiles loaded ahead.
+* Inside the key and query loops (the loops that issue MFMAs), a wait on
+  the vector-memory counter may only come right before a barrier. The tile
+  loads into LDS are inline asm the compiler does not count, so a wait it
+  inserts for a load it does see (say, of Q) would also wait for the tiles
+  loaded ahead. (Loops without MFMAs, such as the copy of a block-sparse
+  row's kept-block list before the first tile load, are not concerned.)
 """
 import os
 import re
@@ -111,6 +113,8 @@ def test_vmcnt_waits_in_loops_only_before_barriers(asm):
         for a, b in loops:
             code = [l.split(";")[0].strip() for l in lines[a:b + 1]]
             code = [l for l in code if l]
+            if not any(l.startswith("v_mfma") for l in code):
+                continue
             for i, l in enumerate(code):
                 if l.startswith("s_waitcnt") and "vmcnt" in l:
                     # the next instruction, skipping labels and the scalar

@@ -401,28 +401,30 @@ def test_merge_all_empty(L):
     assert (o == 0).all() and t.isneginf(lse).all()
 
 
-SPARSE_CASES = [  # (Sq, Skv, H)
-    (128, 128, 1), (300, 257, 2), (640, 1000, 2), (1024, 1024, 3),
+SPARSE_CASES = [  # (Sq, Skv, H, B)
+    (128, 128, 1, 1), (300, 257, 2, 1), (640, 1000, 2, 1), (1024, 1024, 3, 1),
     # last key block holding exactly 64 keys (its second half is empty) and 65
-    (256, 320, 2), (256, 321, 2),
+    (256, 320, 2, 1), (256, 321, 2, 1),
+    # two batch entries with different masks
+    (700, 900, 3, 2),
 ]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("case", SPARSE_CASES, ids=lambda s: "x".join(map(str, s)))
 def test_blocksparse_vs_oracle(L, dtype, case):
-    Sq, Skv, H = case
+    Sq, Skv, H, B = case
     G.announce(f"sparse {dtype} {case}")
     t = G.torch()
-    q, k, v = I.make_custom((1, Sq, H, 128), (1, Skv, H, 128), dtype, seed=Sq + Skv)
+    q, k, v = I.make_custom((B, Sq, H, 128), (B, Skv, H, 128), dtype, seed=Sq + Skv)
     nqb, nkb = -(-Sq // 128), -(-Skv // 128)
     rng = np.random.default_rng(Sq * 31 + Skv)
-    mask = (rng.random((1, H, nqb, nkb)) < 0.4).astype(np.uint8)
+    mask = (rng.random((B, H, nqb, nkb)) < 0.4).astype(np.uint8)
     mask[0, 0, 0, :] = 0          # a query block with no kept key block
     if nkb > 1:
-        mask[0, -1, -1, :] = 0
-        mask[0, -1, -1, nkb - 1] = 1   # only the partial last key block
-    o, lse = G.poisoned_outputs(1, Sq, H)
+        mask[-1, -1, -1, :] = 0
+        mask[-1, -1, -1, nkb - 1] = 1   # only the partial last key block
+    o, lse = G.poisoned_outputs(B, Sq, H)
     L.attn_fwd_blocksparse(G.to_gpu(q, dtype), G.to_gpu(k, dtype), G.to_gpu(v, dtype),
                            t.from_numpy(mask).cuda(), o=o, lse=lse)
     o_ref, lse_ref = oracle.attention_ref(q.values, k.values, v.values, 1 / math.sqrt(128),
