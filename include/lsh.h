@@ -216,10 +216,13 @@ lsh_status lsh_head_permute(const void* src, void* dst, int32_t dtype,
  * workspace: at least lsh_attn_fwd_blocksparse_workspace(args) bytes; it
  * holds the launch schedule, readable after the call for diagnostics. With
  * n = B * H * ceil(Sq/128) items (item = (b * H + h) * ceil(Sq/128) + query
- * block) and R = n * 4 rounded up to 256 bytes:
- *   int32 counts[n]     at byte 0:     kept blocks of each item's mask row;
- *   int32 order[n]      at byte R:     item of each launch slot;
- *   int64 totals[B * H] at byte 2 * R: kept blocks of each head.
+ * block), nk = ceil(Skv/128), R = n * 4 and T = B * H * 8, each rounded up
+ * to 256 bytes:
+ *   int32 counts[n]      at byte 0:         kept blocks of each item's mask row;
+ *   int32 order[n]       at byte R:         item of each launch slot;
+ *   int64 totals[B * H]  at byte 2 * R:     kept blocks of each head;
+ *   uint16 kept[n][nk]   at byte 2 * R + T: each item's kept key blocks,
+ *                                           ascending (counts[item] of them).
  * Heads go in descending total (ties: lower index first) and, inside a
  * head, items in descending count (ties: lower index first). Launch slots
  * are handed to the 8 XCDs in turn, so each XCD works through one head's

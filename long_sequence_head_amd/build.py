@@ -20,10 +20,10 @@ LIBDIR = os.path.join(PKG, "lib")
 LIBNAME = "liblsh.so"
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip", "aux_kernels.hip", "api.hip"]
-# Per-file code generation options. The forward and the dQ kernel keep their
-# MFMA results in VGPRs: the scores feed VALU work directly and the register
-# allocator otherwise shuttles them through AGPRs. The dK/dV kernel
-# (attn_bwd.hip) needs AGPRs for its 128 accumulators and keeps the default.
+# Per-file code generation options. Every attention file keeps MFMA results
+# in VGPRs: the scores feed VALU work directly and the register allocator
+# otherwise shuttles them through AGPRs. The dK/dV kernel (attn_bwd.hip)
+# pins its 128 accumulators to AGPRs through an inline-asm MFMA instead.
 FILE_FLAGS = {"attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
               "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
               "attn_bwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}

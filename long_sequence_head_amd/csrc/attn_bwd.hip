@@ -75,13 +75,16 @@ __global__ __launch_bounds__(256) void attn_bwd_rows_kernel(BwdParams p) {
 // compiled with MFMA results in VGPRs, so that S and dP (which the
 // elementwise step reads) need no copies out of AGPRs; the 128 accumulator
 // registers, which only MFMAs touch inside the loop, are pinned to AGPRs by
-// this asm instead. The compiler's hazard checks do not see into the asm:
-// within the loop an accumulator is reused 8 MFMAs later and its A and B
-// operands were written long before, so no wait states are needed there;
-// mfma_drain() covers the VALU writes before the first MFMA and the reads
-// after the last one.
+// this asm instead. The compiler's hazard checks do not see into the asm,
+// and the compiler may copy the accumulators between AGPRs (loop exits,
+// remainder paths) right before it: the asm therefore starts with two wait
+// states of its own (s_nop 1), which a VALU or v_accvgpr_write of any of
+// its operands needs before an MFMA reads it. On the other side,
+// mfma_drain() separates the last MFMAs from any read of their results;
+// tests/test_codegen.py checks both distances over the kernel's control
+// flow.
 __device__ __forceinline__ void mfma_acc_agpr(f32x16& c, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_drain() {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");

@@ -178,16 +178,18 @@ __device__ __forceinline__ int tile_key0(int t, const unsigned short* kept) {
 // wavefront) then hit every LDS bank once.
 __device__ __forceinline__ int swz_v16(int row, int c) { return c ^ (2 * (row & 7)); }
 
-template <int WAVES, int S, bool SPARSE>
+template <int WAVES, int QG, int S, bool SPARSE>
 __device__ __forceinline__ void attention16(const AttnParams& p) {
-  constexpr int BM = WAVES * kQW;
+  constexpr int RW = 16 * QG;                          // query rows per wavefront
+  constexpr int BM = WAVES * RW;
   constexpr int LPW = (kTileBytes / 1024) / WAVES;   // 1-KiB loads per wavefront per tile
   constexpr int PF = 2;                                // fragment reads ahead, in slots
   constexpr int kSlotBytes = kTileBytes;
   static_assert(LPW * WAVES * 1024 == kTileBytes, "tile/threads mismatch");
   static_assert(S == 2 || S == 3, "2 or 3 slots per ring");
   static_assert(!SPARSE || BM == kMaskBlock, "a sparse workgroup covers one mask row");
-  static_assert(WAVES * 8192 <= 2 * S * kSlotBytes, "epilogue staging must fit the tile slots");
+  static_assert(QG == 1 || QG == 2, "one or two 16-query groups per wavefront");
+  static_assert(WAVES * (8192 + 128) <= 2 * S * kSlotBytes, "epilogue staging must fit the tile slots");
 
   // K slots 0..S-1, then V slots 0..S-1
   __shared__ __attribute__((aligned(1024))) unsigned char lds_buf[2 * S * kSlotBytes];
@@ -203,7 +205,7 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
     item = xcd_remap(blockIdx.x, gridDim.x);
   }
   const Item it = decode_item(item, p.n_qblk, p.H);
-  const int q0 = it.qblk * BM + wave * kQW;   // first query row of the wavefront
+  const int q0 = it.qblk * BM + wave * RW;    // first query row of the wavefront
   const __bf16* qp = static_cast<const __bf16*>(p.q) + it.b * p.q_sb + it.h * p.q_sh;
   const __bf16* kp = static_cast<const __bf16*>(p.k) + it.b * p.k_sb + it.h * p.k_sh;
   const __bf16* vp = static_cast<const __bf16*>(p.v) + it.b * p.v_sb + it.h * p.v_sh;
@@ -219,9 +221,9 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
 
   // Q fragments (B operand of S^T = K Q^T): qf[qg][dc] holds
   // Q[q0 + 16 qg + t][32 dc + 8 g .. +7].
-  bf16x8 qf[2][4];
+  bf16x8 qf[QG][4];
 #pragma unroll
-  for (int qg = 0; qg < 2; ++qg) {
+  for (int qg = 0; qg < QG; ++qg) {
     const int qi = q0 + 16 * qg + t16;
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc)
@@ -318,32 +320,46 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
   };
 
   const float c = p.scale_log2;
-  f32x4 acc[8][2];   // O^T[dg][qg]
+  f32x4 acc[8][QG];   // O^T[dg][qg]
+  float m_run[QG], mc[QG], l_run[QG];
 #pragma unroll
-  for (int dg = 0; dg < 8; ++dg) acc[dg][0] = acc[dg][1] = f32x4{};
-  float m_run[2] = {kNegInf, kNegInf}, mc[2] = {0.0f, 0.0f}, l_run[2] = {0.0f, 0.0f};
-  f32x4 su[2][2][2];   // scores of two consecutive units (by parity): su[parity][kg][qg]
-  bf16x8 pu[2][2];     // P of two consecutive units (by parity): pu[parity][qg]
+  for (int qg = 0; qg < QG; ++qg) {
+#pragma unroll
+    for (int dg = 0; dg < 8; ++dg) acc[dg][qg] = f32x4{};
+    m_run[qg] = kNegInf;
+    mc[qg] = 0.0f;
+    l_run[qg] = 0.0f;
+  }
+  f32x4 su[2][2][QG];   // scores of two consecutive units (by parity): su[parity][kg][qg]
+  bf16x8 pu[2][QG];     // P of two consecutive units (by parity): pu[parity][qg]
 
-  auto mask_unit = [&](f32x4 (&st)[2][2], int kb0) __device__ {
+  auto mask_unit = [&](f32x4 (&st)[2][QG], int kb0) __device__ {
     if (kb0 + 32 > p.Skv) {
       const int lim = p.Skv - kb0 - 4 * g;
 #pragma unroll
       for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (16 * kg + i >= lim) st[kg][0][i] = st[kg][1][i] = kNegInf;
+#pragma unroll
+          for (int qg = 0; qg < QG; ++qg)
+            if (16 * kg + i >= lim) st[kg][qg][i] = kNegInf;
     }
   };
-  // scores i = 2 h and 2 h + 1 of the lane's 8 for query group qg and key
-  // group kg: x = exp2(s c - m c), l += x in key order, P = bf16(x)
-  auto score2 = [&](const f32x4 (&st)[2][2], bf16x8 (&pc)[2], int qg, int kg, int h) __device__ {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int i = 2 * h + q;
-      const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kg][qg][i], c, -mc[qg]));
-      l_run[qg] = l_run[qg] + x;
-      pc[qg][4 * kg + i] = (__bf16)x;
+  // score i of the lane's 8 for query group qg and key group kg:
+  // x = exp2(s c - m c), l += x (in key order over the calls), P = bf16(x)
+  auto score1 = [&](const f32x4 (&st)[2][QG], bf16x8 (&pc)[QG], int qg, int kg, int i) __device__ {
+    const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kg][qg][i], c, -mc[qg]));
+    l_run[qg] = l_run[qg] + x;
+    pc[qg][4 * kg + i] = (__bf16)x;
+  };
+  // the softmax share of slot i (0..7) of a stage: the lane's 8 scores per
+  // query group spread over the 8 slots in key order
+  auto score_slot = [&](const f32x4 (&st)[2][QG], bf16x8 (&pc)[QG], int i) __device__ {
+    if constexpr (QG == 2) {
+      score1(st, pc, i >> 2, (i >> 1) & 1, 2 * (i & 1));
+      score1(st, pc, i >> 2, (i >> 1) & 1, 2 * (i & 1) + 1);
+    } else {
+      score1(st, pc, 0, i >> 2, i & 3);
     }
   };
   auto max4 = [&](float x) __device__ -> float {
@@ -351,14 +367,15 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
     return fmaxf(x, __shfl_xor(x, 32));
   };
   // end of a unit's softmax: the lazy-rescale check (see above)
-  auto unit_check = [&](const f32x4 (&st)[2][2], bf16x8 (&pc)[2], const float (&l0)[2]) __device__ {
-    const bool sure0 = m_run[0] != kNegInf && l_run[0] - l0[0] <= kSureSum;
-    const bool sure1 = m_run[1] != kNegInf && l_run[1] - l0[1] <= kSureSum;
-    if (wave_any(!(sure0 && sure1))) {
-      bool need[2];
-      float mx[2];
+  auto unit_check = [&](const f32x4 (&st)[2][QG], bf16x8 (&pc)[QG], const float (&l0)[QG]) __device__ {
+    bool sure = true;
 #pragma unroll
-      for (int qg = 0; qg < 2; ++qg) {
+    for (int qg = 0; qg < QG; ++qg) sure = sure && m_run[qg] != kNegInf && l_run[qg] - l0[qg] <= kSureSum;
+    if (wave_any(!sure)) {
+      bool need[QG], any_need = false;
+      float mx[QG];
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) {
         float pm = kNegInf;
 #pragma unroll
         for (int kg = 0; kg < 2; ++kg)
@@ -366,10 +383,11 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
           for (int i = 0; i < 4; ++i) pm = fmaxf(pm, st[kg][qg][i]);
         mx[qg] = max4(pm);
         need[qg] = (mx[qg] - m_run[qg]) * c > kRescaleLog2;
+        any_need = any_need || need[qg];
       }
-      if (wave_any(need[0] || need[1])) {
+      if (wave_any(any_need)) {
 #pragma unroll
-        for (int qg = 0; qg < 2; ++qg) {
+        for (int qg = 0; qg < QG; ++qg) {
           const float m_new = need[qg] ? mx[qg] : m_run[qg];
           const float alpha = need[qg] ? __builtin_amdgcn_exp2f((m_run[qg] - m_new) * c) : 1.0f;
           m_run[qg] = m_new;
@@ -378,10 +396,9 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
 #pragma unroll
           for (int dg = 0; dg < 8; ++dg) acc[dg][qg] *= alpha;
 #pragma unroll
-          for (int kg = 0; kg < 2; ++kg) {
-            score2(st, pc, qg, kg, 0);
-            score2(st, pc, qg, kg, 1);
-          }
+          for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) score1(st, pc, qg, kg, i);
         }
       }
     }
@@ -404,10 +421,10 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
   // pu[1]. j0 = t % S (a compile-time constant at every call). Stage B's
   // lazy-rescale check runs at the start of the next tile step (it has to
   // precede only the output MFMAs of unit 2t+2 and the softmax of unit
-  // 2t+3), beside that step's first fragment reads; `check_b` returns the
+  // 2t+3), beside that step's first fragment reads; lb_next returns the
   // sums it needs.
   auto tile_step = [&](int t, int j0, bool has_next, bool ragged, bool pending,
-                       const float (&lb)[2], float (&lb_next)[2]) __device__ {
+                       const float (&lb)[QG], float (&lb_next)[QG]) __device__ {
     const int ks = (j0 + 1) % S, vs = j0 % S;
     bf16x8 kf[16], vf[16];
 #pragma unroll
@@ -418,7 +435,9 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
     // the previous stage B's check: unit 2t (parity 0)
     if (pending) unit_check(su[0], pu[0], lb);
     if (ragged) mask_unit(su[1], key0_of(t) + 32);
-    float la[2] = {l_run[0], l_run[1]};
+    float la[QG];
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) la[qg] = l_run[qg];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -428,20 +447,20 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
         // end of stage A: softmax unit 2t+1 is complete
         unit_check(su[1], pu[1], la);
         if (has_next && ragged) mask_unit(su[0], key0_of(t + 1));
-        la[0] = l_run[0];
-        la[1] = l_run[1];
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) la[qg] = l_run[qg];
         __builtin_amdgcn_sched_barrier(0);
       }
-      f32x4 (&sn)[2][2] = su[par];          // QK target: unit 2t+2+par
-      const bf16x8 (&pp)[2] = pu[par];      // PV source: unit 2t+par
+      f32x4 (&sn)[2][QG] = su[par];         // QK target: unit 2t+2+par
+      const bf16x8 (&pp)[QG] = pu[par];     // PV source: unit 2t+par
       if (has_next) {
 #pragma unroll
-        for (int qg = 0; qg < 2; ++qg)
+        for (int qg = 0; qg < QG; ++qg)
           sn[kg][qg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j], qf[qg][dc],
                                                                dc == 0 ? f32x4{} : sn[kg][qg], 0, 0, 0);
       }
 #pragma unroll
-      for (int qg = 0; qg < 2; ++qg)
+      for (int qg = 0; qg < QG; ++qg)
         acc[i][qg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[j], pp[qg], acc[i][qg], 0, 0, 0);
       if (j + PF < 16) {
         if (has_next) kf[j + PF] = kfrag(ks, j + PF);
@@ -449,9 +468,17 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
       }
       // softmax: stage A exponentiates unit 2t+1 (parity 1), stage B unit
       // 2t+2 (parity 0, only if it exists)
-      if (par == 0) score2(su[1], pu[1], i >> 2, (i >> 1) & 1, i & 1);
-      else if (has_next) score2(su[0], pu[0], i >> 2, (i >> 1) & 1, i & 1);
-      if (has_next) {
+      if (par == 0) score_slot(su[1], pu[1], i);
+      else if (has_next) score_slot(su[0], pu[0], i);
+      if (has_next && QG == 1) {
+        // the slot's order: MFMA, LDS read, 2 VALU, MFMA, 2 LDS reads, 2 VALU
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      } else if (has_next) {
         // the slot's order: MFMA, LDS read, 3 VALU, MFMA, LDS read, MFMA,
         // LDS read, 3 VALU, MFMA, 2 VALU. Left to itself the compiler groups
         // the four MFMAs, and with the two wavefronts of a SIMD in step the
@@ -469,8 +496,8 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    lb_next[0] = la[0];
-    lb_next[1] = la[1];
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) lb_next[qg] = la[qg];
   };
   // end of tile step t: K(t+2) and V(t+1) landed everywhere, then the freed
   // slots are refilled
@@ -495,7 +522,9 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
     barrier_no_fence();
     // Unit 0's scores, then unit 1's scores beside unit 0's softmax (K
     // tile 0; no output yet).
-    float lb[2] = {0.0f, 0.0f};
+    float lb[QG];
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) lb[qg] = 0.0f;
     {
       bf16x8 kf[16];
 #pragma unroll
@@ -509,11 +538,11 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int qg = 0; qg < 2; ++qg)
+        for (int qg = 0; qg < QG; ++qg)
           su[par][kg][qg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               kf[j], qf[qg][dc], dc == 0 ? f32x4{} : su[par][kg][qg], 0, 0, 0);
         if (j + PF < 16) kf[j + PF] = kfrag(0, j + PF);
-        if (par == 1) score2(su[0], pu[0], i >> 2, (i >> 1) & 1, i & 1);
+        if (par == 1) score_slot(su[0], pu[0], i);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -526,10 +555,10 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
     for (; t + S <= n - S - 1; t += S) {
 #pragma unroll
       for (int j = 0; j < S; ++j) {
-        float lb2[2];
+        float lb2[QG];
         tile_step(t + j, j, true, false, true, lb, lb2);
-        lb[0] = lb2[0];
-        lb[1] = lb2[1];
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) lb[qg] = lb2[qg];
         step_end(t + j, true);
       }
     }
@@ -539,14 +568,14 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
 #pragma unroll
     for (int j = 0; j < 2 * S - 1; ++j) {
       if (j + 1 < r) {
-        float lb2[2];
+        float lb2[QG];
         tile_step(t + j, j % S, true, true, true, lb, lb2);
-        lb[0] = lb2[0];
-        lb[1] = lb2[1];
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) lb[qg] = lb2[qg];
         step_end(t + j, false);
       }
     }
-    float lb2[2];
+    float lb2[QG];
     switch ((r - 1) % S) {
       case 0: tile_step(n - 1, 0, false, true, true, lb, lb2); break;
       case 1: tile_step(n - 1, 1 % S, false, true, true, lb, lb2); break;
@@ -558,9 +587,9 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
   // in all four), then O leaves through LDS: each wavefront stages 16 rows
   // x 128 floats of its O per query group (chunk c of row t stored at chunk
   // c ^ t), with the row's 1/l and LSE beside them, and writes whole rows.
-  float l_tot[2], lse_new[2], inv_l[2];
+  float l_tot[QG], lse_new[QG], inv_l[QG];
 #pragma unroll
-  for (int qg = 0; qg < 2; ++qg) {
+  for (int qg = 0; qg < QG; ++qg) {
     const float a2 = l_run[qg] + __shfl_xor(l_run[qg], 16);
     l_tot[qg] = a2 + __shfl_xor(a2, 32);
     const bool empty = !(l_tot[qg] > 0.0f);
@@ -574,7 +603,7 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
   asm volatile("" : "+v"(tid2));
   const int lane2 = tid2 & 63;
 #pragma unroll
-  for (int qg = 0; qg < 2; ++qg) {
+  for (int qg = 0; qg < QG; ++qg) {
 #pragma unroll
     for (int dg = 0; dg < 8; ++dg) {
       const int ch = 4 * dg + g;   // 16-byte chunk of the row
@@ -646,30 +675,34 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
   }
 }
 
-// The three bf16 kernels, one template:
-//  * dense, large grids: 8 wavefronts (256 query rows), one workgroup per
-//    CU, two wavefronts per SIMD, three slots per ring (96 KiB);
+// The three bf16 kernels, one template (same per-query arithmetic, so the
+// same bits):
+//  * dense, large grids: 8 wavefronts of 32 query rows (256 rows), one
+//    workgroup per CU, two wavefronts per SIMD, three slots per ring
+//    (96 KiB);
 //  * dense grids that 256-row workgroups would leave partly idle where
-//    128-row ones would not (a ring round of 4096 queries x 8 heads): 4
-//    wavefronts (128 rows), one wavefront per SIMD;
-//  * block-sparse: 4 wavefronts on one 128-row mask row, two workgroups per
-//    CU (two wavefronts per SIMD, each with its own mask row), two slots per
-//    ring (64 KiB each).
+//    128-row ones would not (a ring round of 4096 queries x 8 heads): 8
+//    wavefronts of 16 rows (128 rows), still two wavefronts per SIMD; each
+//    K and V fragment then feeds one query group instead of two;
+//  * block-sparse: 4 wavefronts of 32 rows on one 128-row mask row, two
+//    workgroups per CU (two wavefronts per SIMD, each with its own mask
+//    row), two slots per ring (64 KiB each).
 constexpr int kP8Waves = 8;
-constexpr int kP8BM = kP8Waves * kQW;
-constexpr int kP4Waves = 4;
-constexpr int kP4BM = kP4Waves * kQW;
+constexpr int kP8BM = kP8Waves * 32;
+constexpr int kH8Waves = 8;
+constexpr int kH8BM = kH8Waves * 16;
+constexpr int kS4Waves = 4;
 
 __global__ __launch_bounds__(kP8Waves * 64, 1) void attn_fwd_bf16_p8_kernel(AttnParams p) {
-  attention16<kP8Waves, 3, false>(p);
+  attention16<kP8Waves, 2, 3, false>(p);
 }
 
-__global__ __launch_bounds__(kP4Waves * 64, 1) void attn_fwd_bf16_p4_kernel(AttnParams p) {
-  attention16<kP4Waves, 3, false>(p);
+__global__ __launch_bounds__(kH8Waves * 64, 1) void attn_fwd_bf16_h8_kernel(AttnParams p) {
+  attention16<kH8Waves, 1, 3, false>(p);
 }
 
-__global__ __launch_bounds__(kP4Waves * 64, 2) void attn_fwd_bf16_s4_kernel(AttnParams p) {
-  attention16<kP4Waves, 2, true>(p);
+__global__ __launch_bounds__(kS4Waves * 64, 2) void attn_fwd_bf16_s4_kernel(AttnParams p) {
+  attention16<kS4Waves, 2, 2, true>(p);
 }
 
 // ------------------------------------------------------------------ f32 path
@@ -834,21 +867,20 @@ hipError_t launch_attn_dense(const AttnParams& p0, DType dt, hipStream_t s) {
     hipLaunchKernelGGL((attn_fwd_f32_kernel<4, false>), dim3(p.n_items), dim3(256), 0, s, p);
     return hipGetLastError();
   }
-  // The 8-wavefront kernel (two wavefronts per SIMD, 256 rows per
-  // workgroup) unless its grid would leave CUs idle where the 4-wavefront
-  // kernel's would not (a ring round of 4096 queries x 8 heads: 128
+  // 256-row workgroups unless their grid would leave CUs idle where the
+  // 128-row one would not (a ring round of 4096 queries x 8 heads: 128
   // workgroups of 256 rows against 256 of 128). Both give the same bits.
   const int64_t p8_items = (int64_t)p.B * p.H * ((p.Sq + kP8BM - 1) / kP8BM);
-  const int64_t p4_items = (int64_t)p.B * p.H * ((p.Sq + kP4BM - 1) / kP4BM);
-  if (prefer_two_waves(p8_items, p4_items, p.n_cu)) {
+  const int64_t h8_items = (int64_t)p.B * p.H * ((p.Sq + kH8BM - 1) / kH8BM);
+  if (prefer_two_waves(p8_items, h8_items, p.n_cu)) {
     p.n_qblk = (p.Sq + kP8BM - 1) / kP8BM;
     p.n_items = (int32_t)p8_items;
     hipLaunchKernelGGL(attn_fwd_bf16_p8_kernel, dim3(p.n_items), dim3(kP8Waves * 64), 0, s, p);
     return hipGetLastError();
   }
-  p.n_qblk = (p.Sq + kP4BM - 1) / kP4BM;
-  p.n_items = (int32_t)p4_items;
-  hipLaunchKernelGGL(attn_fwd_bf16_p4_kernel, dim3(p.n_items), dim3(kP4Waves * 64), 0, s, p);
+  p.n_qblk = (p.Sq + kH8BM - 1) / kH8BM;
+  p.n_items = (int32_t)h8_items;
+  hipLaunchKernelGGL(attn_fwd_bf16_h8_kernel, dim3(p.n_items), dim3(kH8Waves * 64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -860,7 +892,7 @@ hipError_t launch_attn_sparse(const AttnParams& p0, DType dt, hipStream_t s) {
   if (dt == DType::F32)
     hipLaunchKernelGGL((attn_fwd_f32_kernel<4, true>), dim3(p.n_items), dim3(256), dyn, s, p);
   else
-    hipLaunchKernelGGL(attn_fwd_bf16_s4_kernel, dim3(p.n_items), dim3(kP4Waves * 64), dyn, s, p);
+    hipLaunchKernelGGL(attn_fwd_bf16_s4_kernel, dim3(p.n_items), dim3(kS4Waves * 64), dyn, s, p);
   return hipGetLastError();
 }
 

@@ -99,12 +99,11 @@ struct BwdParams {
   int32_t n_cu;       // compute units of the device (0: assume 256)
 };
 
-// Whether a kernel running two wavefronts per SIMD on workgroups of 2R
-// rows (items_big of them) should run rather than one running one
-// wavefront per SIMD on workgroups of R rows (items_small), judged by the
-// rounds each needs over the CUs: a workgroup of the former takes about
-// 5/3 as long as one of the latter (it does twice the work at about 1.2
-// times the rate), so it wins unless its last round leaves many CUs idle.
+// Whether the kernel on workgroups of 2R rows (items_big of them) should
+// run rather than the one on workgroups of R rows (items_small), judged by
+// the rounds each needs over the CUs: a workgroup of the former takes about
+// 5/3 as long as one of the latter (twice the rows at about 1.2 times the
+// rate), so it wins unless its last round leaves many CUs idle.
 inline bool prefer_two_waves(int64_t items_big, int64_t items_small, int n_cu) {
   const int64_t cus = n_cu > 0 ? n_cu : 256;
   const int64_t r_big = (items_big + cus - 1) / cus;

@@ -230,10 +230,3 @@ def attention_bwd_ref(q, k, v, dout, scale, rows=None, keys=None, heads=None):
             dk[b, :, h, :] = dk_acc
             dv[b, :, h, :] = dv_acc
     return dq, dk, dv
-
-
-def attention_bwd_flops(B, H, Sq, Skv, D) -> int:
-    """Algorithmic flop count of one attention backward: the five products
-    S = Q K^T, dV = P^T dO, dP = dO V^T, dQ = dS K and dK = dS^T Q, each
-    2*Sq*Skv*D flops, per batch entry and head."""
-    return 10 * B * H * Sq * Skv * D
