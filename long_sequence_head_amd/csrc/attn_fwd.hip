@@ -10,41 +10,21 @@
 // for Visual Generative Models with Dual-Balanced Sequence Parallelism",
 // Abstract).
 //
-// Design, common to the bf16 kernels (a wavefront owns 32 query rows; the
-// wavefronts of a workgroup share each key tile through LDS):
-//  * Q of the wavefront's 32 rows stays in registers for the whole key loop.
-//  * Key tiles of 64 keys go straight from HBM into LDS slots with
-//    buffer_load ... lds. K rows are XOR-swizzled by 16-byte chunk so the
-//    QK^T operand reads are bank-conflict free; V rows use a different
-//    swizzle matched to the transposing reads below.
-//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: the accumulator puts one
-//    query per lane (lane l and l+32 share query l%32 and split the keys),
-//    so the row max and row sum need one cross-half swap only
-//    (v_permlane32_swap), and the exponentiated scores are already laid
-//    out as the B operand of the next product.
-//  * O^T += V^T P^T on the same MFMA. V^T comes straight from the
-//    row-major V tile with ds_read_b64_tr_b16, which returns, per lane, 4
-//    keys of one head_dim column.
-//  * Online softmax in the log2 domain with a lazy rescale: the running
-//    max only moves when a tile's max exceeds it by more than 2^8 in
-//    probability, so P stays <= 256 and the O rescale is skipped on almost
-//    every tile. Each query's arithmetic depends only on its own scores,
-//    in an order fixed per query, so results do not depend on the kernel
-//    chosen, the workgroup size, the grid order, the number of heads or the
-//    strides.
-// Three bf16 kernels, two wavefronts per SIMD where the grid allows:
-//  * dense: eight wavefronts per workgroup (256 query rows), one workgroup
-//    per CU, each wavefront a plain loop over the key tiles; the SIMD
-//    overlaps one wavefront's softmax with the other's MFMAs;
-//  * block-sparse: the same plain loop with four wavefronts (one 128-row
-//    mask row) and two workgroups per CU;
-//  * dense grids that 256-row workgroups would leave partly idle where
-//    128-row ones would not (a ring round): four wavefronts, one per SIMD,
-//    each software-pipelining its key loop (matrix work of one tile
-//    interleaved with the softmax work of its neighbour).
-// fp32 inputs use v_mfma_f32_32x32x2_f32 with the same structure and P kept
-// in fp32. Every kernel writes a row through store_row, which can also fold
-// the row into a running (O, LSE) instead of overwriting it.
+// Two kernel families, both blockwise online softmax over 64-key tiles
+// staged in LDS, with the running row max and sum in registers and fp32 O
+// and LSE out:
+//  * bf16 inputs: one template (attention16 below) on
+//    v_mfma_f32_16x16x32_bf16, key tiles filled by LDS DMA into rings of
+//    slots, a software pipeline of 32-key units per wavefront; three
+//    instances (dense 256-row and 128-row workgroups, block-sparse) that
+//    give the same bits;
+//  * fp32 inputs: one template (attn_fwd_f32_kernel) on
+//    v_mfma_f32_32x32x2_f32, the key tiles of a query block split between
+//    two wavefronts and merged at the end; dense and block-sparse give the
+//    same bits.
+// The exponentials work in the log2 domain with a lazy rescale: the
+// running max only moves when a score passes it by more than 2^8 in
+// probability, so the O rescale is skipped on almost every tile.
 #include "attn_common.hpp"
 
 #include <cstring>
@@ -59,55 +39,6 @@ constexpr float kRescaleLog2 = 8.0f;
 // A tile sum of exp2(s c - m c) within this bound proves every term below
 // 2^7, so no score can trigger the rescale (which needs a term above 2^8).
 constexpr float kSureSum = 128.0f;
-
-// Writes a query row's O (this lane's half: head_dim 32 db + 8 g4 + 4 hh
-// .. +3, from the accumulator acc and the row sum l_tot) and, from the lane
-// with hh = 0, its LSE. With p.accumulate set, the row's (O, LSE) so far is
-// read first and merged with this key block's, as two parts of a key
-// partition merge:
-//   M = max(LSE_old, LSE_new), w = exp(LSE - M), Z = w_old + w_new,
-//   O = (w_old O_old + w_new O_new) / Z, LSE = M + log Z;
-// a row whose two LSE are both -inf is left as it is. Each lane reads only
-// the O chunks it writes, and both lanes of a row read the LSE before
-// either writes it (one load instruction for the wavefront).
-__device__ __forceinline__ void store_row(const AttnParams& p, float* op, float* lsep, int hh,
-                                          float l_tot, float m_run, const f32x16 (&acc)[4]) {
-  const bool empty = !(l_tot > 0.0f);
-  const float inv_l = empty ? 0.0f : 1.0f / l_tot;
-  const float lse = empty ? kNegInf : m_run * p.scale + __logf(l_tot);
-  if (!p.accumulate) {
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = db * 32 + 8 * g4 + 4 * hh;
-        f32x4 o4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o4[i] = acc[db][4 * g4 + i] * inv_l;
-        *reinterpret_cast<f32x4*>(op + d) = o4;
-      }
-    if (hh == 0) *lsep = lse;
-    return;
-  }
-  const float lse_old = *lsep;
-  const float mx = fmaxf(lse_old, lse);
-  if (mx == kNegInf) return;
-  const float w_old = __expf(lse_old - mx), w_new = __expf(lse - mx);
-  const float z = w_old + w_new;
-  const float a_old = w_old / z, a_new = w_new / z * inv_l;
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = db * 32 + 8 * g4 + 4 * hh;
-      const f32x4 old = *reinterpret_cast<const f32x4*>(op + d);
-      f32x4 o4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o4[i] = __builtin_fmaf(acc[db][4 * g4 + i], a_new, old[i] * a_old);
-      *reinterpret_cast<f32x4*>(op + d) = o4;
-    }
-  if (hh == 0) *lsep = mx + __logf(z);
-}
 
 // Copies the ascending list of kept key blocks of one mask row (left in
 // the workspace by the schedule kernels) into LDS. Returns their number.
@@ -706,51 +637,88 @@ __global__ __launch_bounds__(kS4Waves * 64, 2) void attn_fwd_bf16_s4_kernel(Attn
 }
 
 // ------------------------------------------------------------------ f32 path
+//
+// One template for dense and block-sparse fp32, v_mfma_f32_32x32x2_f32 for
+// both products (S^T = K Q^T, O^T += V^T P^T). A workgroup of four
+// wavefronts owns 64 query rows: wavefront w takes query block w / 2 (32
+// rows) and the key tiles t with t % 2 = w % 2 (64-key tiles; for a block
+// mask the two halves of every kept 128-key block). A round stages the
+// tiles 2r and 2r + 1 side by side in LDS and each wavefront runs the online
+// softmax over its own one; afterwards the two halves of a query block
+// merge their running max, sums and outputs through LDS,
+//   m = max(m0, m1), a_i = exp2((m_i - m) c), l = a0 l0 + a1 l1,
+//   O = a0 O0 + a1 O1,
+// the merge of two partial results over disjoint key sets. The split
+// depends on nothing but the key tiles, so neither the grid nor the mask
+// path changes a bit (an all-ones mask gives the dense bits). Twice the
+// wavefronts of one-wavefront-per-32-rows for the same rows: a small problem
+// (4 x 32 heads of 128 queries) fills every SIMD instead of half the CUs.
+//
+// Data movement: Q enters once per workgroup through LDS with 16-byte
+// loads; in the QK^T product lane (r, hh) feeds head-dim element 64 hh + s
+// at step s (any bijection of the 128 elements onto the 64 steps x 2 lane
+// halves gives the same sum terms), so K and Q come out of LDS 16 bytes per
+// read. The V loads of a round are in flight while QK^T runs; O leaves
+// through LDS as whole 512-byte rows.
+constexpr int kF32Row = kD + 4;            // padded LDS row (floats)
+constexpr int kF32Waves = 4;
+constexpr int kF32BM = 64;                 // query rows per workgroup
+constexpr int kF32Tile = kBN * kF32Row;    // floats of one staged tile
 
-// LDS row stride (floats) of the fp32 tiles: padded against bank conflicts.
-constexpr int kF32Row = kD + 4;
-
-template <int WAVES, bool SPARSE>
-__global__ __launch_bounds__(WAVES * 64) void attn_fwd_f32_kernel(AttnParams p) {
-  constexpr int NT = WAVES * 64;
-  constexpr int BM = WAVES * kQW;
-  static_assert(!SPARSE || BM == kMaskBlock, "sparse kernel works on one mask row");
-
-  __shared__ __attribute__((aligned(16))) float lds_k[kBN * kF32Row];
-  __shared__ __attribute__((aligned(16))) float lds_v[kBN * kF32Row];
+template <bool SPARSE>
+__global__ __launch_bounds__(kF32Waves * 64, 1) void attn_fwd_f32_kernel(AttnParams p) {
+  constexpr int NT = kF32Waves * 64;
+  // K tiles of the two halves, then V tiles (132 KiB); Q passes through the
+  // V half first, and the epilogue reuses all of it
+  __shared__ __attribute__((aligned(16))) float lds[4 * kF32Tile];
   extern __shared__ unsigned short kept_dyn[];
-  __shared__ int wave_cnt[WAVES];
+  float* const lds_k = lds;
+  float* const lds_v = lds + 2 * kF32Tile;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
+  const int qb = wave >> 1, half = wave & 1;
 
-  int item;
+  int item, row0;   // first query row of the workgroup
   if constexpr (SPARSE) {
-    item = p.order ? p.order[blockIdx.x] : (int)blockIdx.x;
+    // two workgroups per 128-row mask row
+    const int wg = (int)(blockIdx.x >> 1);
+    item = p.order ? p.order[wg] : wg;
+    row0 = decode_item(item, p.n_qblk, p.H).qblk * kMaskBlock + (int)(blockIdx.x & 1) * kF32BM;
   } else {
     item = xcd_remap(blockIdx.x, gridDim.x);
+    row0 = decode_item(item, p.n_qblk, p.H).qblk * kF32BM;
   }
   const Item it = decode_item(item, p.n_qblk, p.H);
-  const int qi = it.qblk * BM + wave * kQW + l32;
-  const bool q_ok = qi < p.Sq;
-
   const float* qp = static_cast<const float*>(p.q) + it.b * p.q_sb + it.h * p.q_sh;
   const float* kp = static_cast<const float*>(p.k) + it.b * p.k_sb + it.h * p.k_sh;
   const float* vp = static_cast<const float*>(p.v) + it.b * p.v_sb + it.h * p.v_sh;
 
   int n_tiles;
-  const unsigned short* kept = kept_dyn;
   if constexpr (SPARSE) {
     n_tiles = 2 * load_kept_list<NT>(p, item, kept_dyn);
   } else {
     n_tiles = (p.Skv + kBN - 1) / kBN;
   }
+  auto key0_of = [&](int t) __device__ -> int { return tile_key0<SPARSE>(t, kept_dyn); };
 
-  // Q: lane holds Q[qi][2 s + hh], s = 0..63
-  float qf[64];
+  // Loads are branch-free, so that all of a thread's loads are in flight at
+  // once: a row past the end reads the last row instead (a query row that is
+  // never written; a key whose score is masked to -inf, so that its V row is
+  // weighted by exactly 0).
+  // Q rows of the workgroup: 64 rows x 32 chunks, 8 per thread
+  f32x4 qr[8];
 #pragma unroll
-  for (int s = 0; s < 64; ++s) qf[s] = q_ok ? qp[(int64_t)qi * p.q_ss + 2 * s + hh] : 0.0f;
+  for (int u = 0; u < 8; ++u) {
+    const int cid = tid + u * NT, row = min(row0 + (cid >> 5), p.Sq - 1), ch = cid & 31;
+    qr[u] = *reinterpret_cast<const f32x4*>(qp + (int64_t)row * p.q_ss + 4 * ch);
+  }
+  // key row of tile t (a tile past the last one reads the last one)
+  auto key_row = [&](int t, int row) __device__ -> int64_t {
+    return min(key0_of(min(t, n_tiles - 1)) + row, p.Skv - 1);
+  };
 
+  float qf[64];      // Q[row][64 hh + s]
   f32x16 acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -759,87 +727,215 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_f32_kernel(AttnParams p) 
   float m_run = kNegInf, l_run = 0.0f;
   const float c = p.scale_log2;
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int key0 = tile_key0<SPARSE>(t, kept);
-    // stage the tile: 64 rows x 32 float4 chunks per tensor
-    for (int cid = tid; cid < kBN * (kD / 4); cid += NT) {
-      const int row = cid >> 5, ch = cid & 31;
-      const int key = key0 + row;
-      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-      if (key < p.Skv) {
-        kv = *reinterpret_cast<const f32x4*>(kp + (int64_t)key * p.k_ss + ch * 4);
-        vv = *reinterpret_cast<const f32x4*>(vp + (int64_t)key * p.v_ss + ch * 4);
+  // one round: tiles r0 and r0 + 1 (chunk u of a thread: tile u / 8, row
+  // (cid / 32) % 64, 16-byte chunk cid % 32 with cid = tid + 256 u)
+  auto round = [&](int r0, auto first) __device__ {
+    f32x4 kr[16], vr[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int cid = tid + u * NT, hf = cid >> 11, row = (cid >> 5) & 63, ch = cid & 31;
+      kr[u] = *reinterpret_cast<const f32x4*>(kp + key_row(r0 + hf, row) * p.k_ss + 4 * ch);
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int cid = tid + u * NT, hf = cid >> 11, row = (cid >> 5) & 63, ch = cid & 31;
+      vr[u] = *reinterpret_cast<const f32x4*>(vp + key_row(r0 + hf, row) * p.v_ss + 4 * ch);
+    }
+    if constexpr (decltype(first)::value) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int cid = tid + u * NT, row = cid >> 5, ch = cid & 31;
+        *reinterpret_cast<f32x4*>(&lds_v[row * kF32Row + 4 * ch]) = qr[u];
       }
-      *reinterpret_cast<f32x4*>(&lds_k[row * kF32Row + ch * 4]) = kv;
-      *reinterpret_cast<f32x4*>(&lds_v[row * kF32Row + ch * 4]) = vv;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int cid = tid + u * NT, hf = cid >> 11, row = (cid >> 5) & 63, ch = cid & 31;
+      *reinterpret_cast<f32x4*>(&lds_k[hf * kF32Tile + row * kF32Row + 4 * ch]) = kr[u];
     }
     __syncthreads();
-
-    f32x16 st[2];
+    if constexpr (decltype(first)::value) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int j = 0; j < 16; ++j) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(&lds_v[(qb * kQW + l32) * kF32Row + 64 * hh + 4 * j]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[kb][r] = 0.0f;
-      const int row = kb * 32 + l32;
-#pragma unroll
-      for (int s = 0; s < 64; ++s)
-        st[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(lds_k[row * kF32Row + 2 * s + hh], qf[s],
-                                                      st[kb], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) qf[4 * j + i] = a[i];
+      }
     }
-    if (key0 + kBN > p.Skv) {
+    const int t = r0 + half;
+    const int key0 = t < n_tiles ? key0_of(t) : p.Skv;
+    const bool has = key0 < p.Skv;
+    f32x16 st[2];
+    if (has) {
+      const float* tk = lds_k + half * kF32Tile;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[kb][r] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(&tk[(kb * 32 + l32) * kF32Row + 64 * hh + 4 * j]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            st[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], qf[4 * j + i], st[kb], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();   // Q (first round) has been read out of the V half
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int cid = tid + u * NT, hf = cid >> 11, row = (cid >> 5) & 63, ch = cid & 31;
+      *reinterpret_cast<f32x4*>(&lds_v[hf * kF32Tile + row * kF32Row + 4 * ch]) = vr[u];
+    }
+    __syncthreads();
+    if (has) {
+      // key of accumulator register r of half hh: kb*32 + 8 (r/4) + 4 hh + r%4
+      if (key0 + kBN > p.Skv) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (key >= p.Skv) st[kb][r] = kNegInf;
+          }
+      }
+      float mx = st[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
+      mx = pair_max(mx);
+      const bool need = (mx - m_run) * c > kRescaleLog2;
+      if (wave_any(need)) {
+        const float m_new = need ? mx : m_run;
+        const float alpha = need ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.0f;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      const float mc = (m_run == kNegInf) ? 0.0f : m_run * c;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key >= p.Skv) st[kb][r] = kNegInf;
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][r], c, -mc));
+          l_run += e;
+          st[kb][r] = e;
+        }
+      // O^T += V^T P^T, one key per lane half and MFMA step
+      const float* tv = lds_v + half * kF32Tile;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(tv[row * kF32Row + db * 32 + l32], st[kb][r],
+                                                           acc[db], 0, 0, 0);
         }
     }
-    float mx = st[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
-    mx = pair_max(mx);
-    const bool need = (mx - m_run) * c > kRescaleLog2;
-    if (wave_any(need)) {
-      const float m_new = need ? mx : m_run;
-      const float alpha = need ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.0f;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-    }
-    const float mc = (m_run == kNegInf) ? 0.0f : m_run * c;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][r], c, -mc));
-        l_run += e;
-        st[kb][r] = e;
-      }
-    // O^T += V^T P^T, one key per MFMA step: half hh uses key
-    // kb*32 + 8 (r/4) + 4 hh + r%4, the key its register r holds.
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(lds_v[row * kF32Row + db * 32 + l32],
-                                                         st[kb][r], acc[db], 0, 0, 0);
-      }
     __syncthreads();
-  }
+  };
 
-  const float l_tot = pair_sum(l_run);
-  if (!q_ok) return;
-  store_row(p, p.o + it.b * p.o_sb + it.h * p.o_sh + (int64_t)qi * p.o_ss,
-            p.lse + it.b * p.lse_sb + it.h * p.lse_sh + qi, hh, l_tot, m_run, acc);
+  if (n_tiles > 0) round(0, std::integral_constant<bool, true>{});
+  for (int r0 = 2; r0 < n_tiles; r0 += 2) round(r0, std::integral_constant<bool, false>{});
+
+  // ---- merge the two halves of each query block: the odd half hands its
+  // accumulators, max and sum to the even half through LDS
+  float* xch = lds_k + qb * (66 * 64);
+  if (half == 1) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xch[(db * 16 + r) * 64 + lane] = acc[db][r];
+    xch[64 * 64 + lane] = m_run;
+    xch[65 * 64 + lane] = l_run;
+  }
+  __syncthreads();
+  // O rows normalised into LDS (32 x kF32Row floats per query block), the
+  // LSE of row r at lse_row[r]
+  float* stg = lds_v + qb * (kQW * kF32Row);
+  float* lse_row = lds_v + 2 * kQW * kF32Row + qb * kQW;
+  if (half == 0) {
+    const float m1 = xch[64 * 64 + lane], l1 = xch[65 * 64 + lane];
+    const float m = fmaxf(m_run, m1);
+    const float a0 = m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f((m_run - m) * c);
+    const float a1 = m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f((m1 - m) * c);
+    const float l_tot = pair_sum(__builtin_fmaf(l_run, a0, l1 * a1));
+    const bool empty = !(l_tot > 0.0f);
+    const float inv_l = empty ? 0.0f : 1.0f / l_tot;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f32x4 o4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * g4 + i;
+          o4[i] = __builtin_fmaf(acc[db][r], a0, xch[(db * 16 + r) * 64 + lane] * a1) * inv_l;
+        }
+        *reinterpret_cast<f32x4*>(&stg[l32 * kF32Row + db * 32 + 8 * g4 + 4 * hh]) = o4;
+      }
+    if (hh == 0) lse_row[l32] = empty ? kNegInf : m * p.scale + __logf(l_tot);
+  }
+  __syncthreads();
+
+  // wavefront (qb, half) writes rows 16 half .. +15 of query block qb, two
+  // whole rows per store instruction. With p.accumulate set, the row's
+  // (O, LSE) so far is read first and merged with this call's, as two
+  // parts of a key partition: M = max(LSE_old, LSE_new), w = exp(LSE - M),
+  // Z = w_old + w_new, O = (w_old O_old + w_new O_new) / Z, LSE = M + log Z;
+  // a row whose two LSE are both -inf is left as it is.
+  float* obase = p.o + it.b * p.o_sb + it.h * p.o_sh;
+  float* lbase = p.lse + it.b * p.lse_sb + it.h * p.lse_sh;
+  const int qrow0 = row0 + qb * kQW + 16 * half;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int row = 16 * half + 2 * k + hh, ch = l32;
+    const int qi = qrow0 + 2 * k + hh;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(&stg[row * kF32Row + 4 * ch]);
+    const float ln = lse_row[row];
+    if (qi < p.Sq) {
+      float* op = obase + (int64_t)qi * p.o_ss + 4 * ch;
+      if (!p.accumulate) {
+        *reinterpret_cast<f32x4*>(op) = a;
+      } else {
+        const float lo = lbase[qi];
+        const float mx = fmaxf(lo, ln);
+        if (mx != kNegInf) {
+          const float w_old = __expf(lo - mx), w_new = __expf(ln - mx);
+          const float z = w_old + w_new;
+          const float a_old = w_old / z, a_new = w_new / z;
+          const f32x4 old = *reinterpret_cast<const f32x4*>(op);
+          f32x4 o4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o4[i] = __builtin_fmaf(a[i], a_new, old[i] * a_old);
+          *reinterpret_cast<f32x4*>(op) = o4;
+        }
+      }
+    }
+  }
+  // LSE: lanes 0..15 write the wavefront's 16 rows (every lane of a row has
+  // read the old LSE above before any lane writes it)
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  if (lane < 16) {
+    const int qi = qrow0 + lane;
+    if (qi < p.Sq) {
+      const float ln = lse_row[16 * half + lane];
+      if (!p.accumulate) {
+        lbase[qi] = ln;
+      } else {
+        const float lo = lbase[qi];
+        const float mx = fmaxf(lo, ln);
+        if (mx != kNegInf) lbase[qi] = mx + __logf(__expf(lo - mx) + __expf(ln - mx));
+      }
+    }
+  }
 }
 
 // O = 0, LSE = -inf for every row (attention over an empty key set).
@@ -862,9 +958,9 @@ __global__ void attn_empty_kernel(AttnParams p) {
 hipError_t launch_attn_dense(const AttnParams& p0, DType dt, hipStream_t s) {
   AttnParams p = p0;
   if (dt == DType::F32) {
-    p.n_qblk = (p.Sq + 127) / 128;
+    p.n_qblk = (p.Sq + kF32BM - 1) / kF32BM;
     p.n_items = p.B * p.H * p.n_qblk;
-    hipLaunchKernelGGL((attn_fwd_f32_kernel<4, false>), dim3(p.n_items), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(attn_fwd_f32_kernel<false>, dim3(p.n_items), dim3(kF32Waves * 64), 0, s, p);
     return hipGetLastError();
   }
   // 256-row workgroups unless their grid would leave CUs idle where the
@@ -889,8 +985,8 @@ hipError_t launch_attn_sparse(const AttnParams& p0, DType dt, hipStream_t s) {
   p.n_qblk = p.n_mqb;
   p.n_items = p.B * p.H * p.n_mqb;
   const size_t dyn = sizeof(unsigned short) * (size_t)p.n_mkb;
-  if (dt == DType::F32)
-    hipLaunchKernelGGL((attn_fwd_f32_kernel<4, true>), dim3(p.n_items), dim3(256), dyn, s, p);
+  if (dt == DType::F32)   // two 64-row workgroups per mask row
+    hipLaunchKernelGGL(attn_fwd_f32_kernel<true>, dim3(2 * p.n_items), dim3(kF32Waves * 64), dyn, s, p);
   else
     hipLaunchKernelGGL(attn_fwd_bf16_s4_kernel, dim3(p.n_items), dim3(kS4Waves * 64), dyn, s, p);
   return hipGetLastError();

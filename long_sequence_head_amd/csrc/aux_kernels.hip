@@ -60,6 +60,13 @@ __global__ __launch_bounds__(kPermThreads) void head_permute_kernel(
 // Distributed Communication Bottlenecks", section on the communication
 // bottleneck). One (b, s, h) row of 128 floats per 32 lanes, float4 each;
 // consecutive rows are contiguous in O.
+//
+// HBM-bound: a lane issues the loads of a whole group of up to kMergeGroup
+// partials (their LSE and its 16 bytes of each O) before it uses any of
+// them, so one memory round trip serves the group. Groups after the first
+// fold in with the running max: when a group raises M, what was summed so
+// far is scaled by exp(M_old - M_new). The sums run over k = 0, 1, ... in
+// order.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeGroup = 8;
 
@@ -78,40 +85,49 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(
   const int64_t lse_off = ((int64_t)b * H + h) * Sq + s;  // within one part
   const int64_t lse_step = (int64_t)B * H * Sq;
   const int64_t o_step = (int64_t)rows * kD;
+  const f32x4* op = reinterpret_cast<const f32x4*>(o_parts + (int64_t)row * kD) + l;
 
-  float M = kNegInf;
-  for (int k = 0; k < n; ++k) M = fmaxf(M, lse_parts[k * lse_step + lse_off]);
+  float M = kNegInf, Z = 0.0f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < n; k0 += kMergeGroup) {
+    // Every slot of the group loads (slots past the last partial reload
+    // that one and get weight 0 through LSE = -inf): branch-free, so the
+    // loads are all in flight at once.
+    f32x4 ok[kMergeGroup];
+    float w[kMergeGroup];
+#pragma unroll
+    for (int j = 0; j < kMergeGroup; ++j) {
+      const int kk = k0 + j < n ? k0 + j : n - 1;
+      w[j] = lse_parts[kk * lse_step + lse_off];
+      ok[j] = __builtin_nontemporal_load(op + kk * (o_step / 4));
+    }
+#pragma unroll
+    for (int j = 0; j < kMergeGroup; ++j) w[j] = k0 + j < n ? w[j] : kNegInf;
+    float mg = kNegInf;
+#pragma unroll
+    for (int j = 0; j < kMergeGroup; ++j) mg = fmaxf(mg, w[j]);
+    // Branch-free, so that nothing holds the loads back: while every part
+    // so far is empty (M = -inf) the exponents use 0 and every weight is 0;
+    // r is exactly 1 when the group does not raise M.
+    const float m_new = fmaxf(M, mg);
+    const float m_use = m_new == kNegInf ? 0.0f : m_new;
+    const float r = __expf(M - m_use);
+    Z *= r;
+    acc *= r;
+    M = m_new;
+#pragma unroll
+    for (int j = 0; j < kMergeGroup; ++j) {
+      const float wj = __expf(w[j] - m_use);   // 0 for an empty part or a padding slot
+      acc += wj * ok[j];
+      Z += wj;
+    }
+  }
   float out_lse = kNegInf;
   if (M != kNegInf) {
-    // Partials in groups of kMergeGroup: all loads of a group are issued
-    // before any is used, so many bytes are in flight per lane; the sums
-    // still run over k = 0, 1, ... in order.
-    float Z = 0.0f;
-    for (int k0 = 0; k0 < n; k0 += kMergeGroup) {
-      f32x4 ok[kMergeGroup];
-      float w[kMergeGroup];
-#pragma unroll
-      for (int j = 0; j < kMergeGroup; ++j) {
-        if (k0 + j < n) {
-          w[j] = lse_parts[(k0 + j) * lse_step + lse_off];
-          ok[j] = __builtin_nontemporal_load(
-              reinterpret_cast<const f32x4*>(o_parts + (k0 + j) * o_step + (int64_t)row * kD) + l);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < kMergeGroup; ++j) {
-        if (k0 + j < n) {
-          const float wj = expf(w[j] - M);
-          acc += wj * ok[j];
-          Z += wj;
-        }
-      }
-    }
     acc *= 1.0f / Z;
-    out_lse = M + logf(Z);
+    out_lse = M + __logf(Z);
   }
-  reinterpret_cast<f32x4*>(o + (int64_t)row * kD)[l] = acc;
+  __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(o + (int64_t)row * kD) + l);
   if (l == 0) lse[lse_off] = out_lse;
 }
 

@@ -435,12 +435,16 @@ def test_blocksparse_vs_oracle(L, dtype, case):
             sigma=sig)
 
 
-def test_blocksparse_all_ones_equals_dense_bitwise(L):
-    G.announce("sparse all-ones")
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_blocksparse_all_ones_equals_dense_bitwise(L, dtype):
+    """Both dtypes: the block-sparse kernel over an all-ones mask keeps the
+    dense kernel's keys per wavefront in the same order (the fp32 kernel
+    also splits them between the same two wavefronts)."""
+    G.announce(f"sparse all-ones {dtype}")
     t = G.torch()
     Sq, Skv, H = 700, 650, 3
-    q, k, v = I.make_custom((1, Sq, H, 128), (1, Skv, H, 128), "bf16", seed=91)
-    qg, kg, vg = G.to_gpu(q, "bf16"), G.to_gpu(k, "bf16"), G.to_gpu(v, "bf16")
+    q, k, v = I.make_custom((1, Sq, H, 128), (1, Skv, H, 128), dtype, seed=91)
+    qg, kg, vg = G.to_gpu(q, dtype), G.to_gpu(k, dtype), G.to_gpu(v, dtype)
     mask = t.ones((1, H, 6, 6), dtype=t.uint8, device="cuda")
     o1, l1 = L.attn_fwd_blocksparse(qg, kg, vg, mask)
     o2, l2 = L.attn_fwd(qg, kg, vg)
