@@ -14,7 +14,10 @@ block-sparse workload (S=32768, 128x128 mask, per-head density
 U[0.1,0.6)), the small fp32 case (B=4, S=128, H=32) and the backward
 (dQ, dK, dV) of the dense forward at S=32760, H=40. Inputs are the seeded
 synthetic tensors of lsh_inputs, resident in HBM before timing. `cpu_baseline` times the fp64 oracle on a
-bounded sample of the headline workload on the host cores.
+bounded sample of the headline workload on the host cores; each secondary
+workload carries its own `cpu_baseline`, the oracle on a labelled sample of
+that workload (or all of it, for the fp32 case) with the GPU's outputs on the
+sample compared against it.
 """
 from __future__ import annotations
 
@@ -88,7 +91,10 @@ def timed(fn, steps, warmup):
 
 
 def flush_l2_mall(buf):
-    buf.fill_(1.0)   # 512 MiB write evicts L2 and the 256 MiB Infinity Cache
+    """Reads 512 MiB: evicts L2 and the 256 MiB Infinity Cache and leaves
+    only clean lines (a write-based flush leaves dirty lines whose
+    write-back would fall into the next timed call)."""
+    buf.sum()
 
 
 # ------------------------------------------------------------------ workloads
@@ -110,12 +116,13 @@ def bench_dense(L, I, w, steps, warmup):
                 matrix_peak_tflops=peak), (q, k, v, o, lse)
 
 
-def bench_chunked(L, I, w, steps, warmup):
+def bench_chunked(L, I, w, steps, warmup, cpu_s=0.0):
     import torch
     log(f"[bench] workload {w.wid}: {w.name}: generating inputs")
     q, k, v = I.make_qkv(w, seed=0)
     qg, kg, vg = upload(q, w.dtype), upload(k, w.dtype), upload(v, w.dtype)
-    del q, k, v
+    if cpu_s <= 0:
+        del q, k, v
     o = torch.empty((w.B, w.Sq, w.H, w.D), dtype=torch.float32, device="cuda")
     lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device="cuda")
     ws = torch.empty(L.chunked_workspace_bytes(qg, kg, vg) + 256, dtype=torch.uint8, device="cuda")
@@ -137,16 +144,37 @@ def bench_chunked(L, I, w, steps, warmup):
              chunks=chunks)
     log(f"[bench] workload {w.wid}: pipeline {ms_pipe:.3f} ms ({r['pipeline_tflops']:.1f} TFLOP/s), "
         f"unchunked {ms_attn:.3f} ms, permute Q+K+V {ms_perm:.3f} ms ({r['permute_GBs']:.0f} GB/s)")
+    if cpu_s > 0:
+        import numpy as np
+        import oracle
+        L.attn_fwd_chunked(qg, kg, vg, chunks, o=o, lse=lse, workspace=ws)
+        torch.cuda.synchronize()
+        heads = [0, w.H - 1]    # first and last chunk
+
+        def run(n):
+            og = o[:, :n][:, :, heads].cpu().numpy()
+            lg = lse[:, heads][:, :, :n].cpu().numpy()
+            o_ref, l_ref = oracle.attention_ref(q.values[:, :n], k.values, v.values, w.scale, heads=heads)
+            return (4 * w.B * len(heads) * n * w.Skv * w.D,
+                    _errs(og, o_ref[:, :, heads], lg, l_ref[:, heads]))
+        r["cpu_baseline"] = oracle_leg(
+            run, 256, w.Sq, 256, cpu_s,
+            lambda n: f"query rows 0..{n - 1} of heads {heads} (first and last chunk) against all "
+                      f"{w.Skv} keys, compared with the chunked pipeline's output",
+            r["pipeline_tflops"])
+        log_leg(w, r["cpu_baseline"])
     return r
 
 
-def bench_ring(L, I, w, steps, warmup):
+def bench_ring(L, I, w, steps, warmup, cpu_s=0.0):
     import torch
     log(f"[bench] workload {w.wid}: {w.name}: generating inputs")
     q, k, v = I.make_qkv(w, seed=0)
     qg, kg, vg = upload(q, w.dtype), upload(k, w.dtype), upload(v, w.dtype)
-    del q, k, v
-    n, blk = w.kv_blocks, w.Skv // w.kv_blocks
+    if cpu_s <= 0:
+        del q, k, v
+    n_blk = n = w.kv_blocks
+    blk = w.Skv // w.kv_blocks
     o_parts = torch.empty((n, w.B, w.Sq, w.H, w.D), dtype=torch.float32, device="cuda")
     l_parts = torch.empty((n, w.B, w.H, w.Sq), dtype=torch.float32, device="cuda")
     o = torch.empty((w.B, w.Sq, w.H, w.D), dtype=torch.float32, device="cuda")
@@ -174,8 +202,28 @@ def bench_ring(L, I, w, steps, warmup):
     ms_step, _ = timed(step, steps, warmup)
     ms_part, _ = timed(partials, steps, warmup)
     ms_online, _ = timed(step_online, steps, warmup)
-    # merge from HBM: flush L2 and the Infinity Cache before each timed call
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    # merge from HBM, two ways. (1) Back to back over four copies of the
+    # partials and outputs (4 x 152 MB, beyond the 256 MiB Infinity Cache):
+    # each call's inputs were evicted by the three calls since their last
+    # use, and the calls are queued without gaps. (2) One call at a time
+    # after a read of 512 MiB that evicts L2 and the Infinity Cache without
+    # leaving dirty lines behind; this includes each call's launch gap.
+    sets = [(o_parts, l_parts, o, lse)] + [
+        (o_parts.clone(), l_parts.clone(), torch.empty_like(o), torch.empty_like(lse)) for _ in range(3)]
+    merge_set = lambda s: L.lse_merge(s[0], s[1], o=s[2], lse=s[3])
+    for s in sets:
+        merge_set(s)
+    torch.cuda.synchronize()
+    reps = 4 * max(4, steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        merge_set(sets[i % 4])
+    e1.record()
+    torch.cuda.synchronize()
+    ms_merge = e0.elapsed_time(e1) / reps
+    del sets
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")   # 512 MiB
     times = []
     for i in range(warmup + steps):
         flush_l2_mall(flush)
@@ -186,15 +234,43 @@ def bench_ring(L, I, w, steps, warmup):
         torch.cuda.synchronize()
         if i >= warmup:
             times.append(e0.elapsed_time(e1))
-    ms_merge = sum(times) / len(times)
+    ms_merge_single = sum(times) / len(times)
     flops = 4 * w.B * w.H * w.Sq * w.Skv * w.D
     mbytes = (o_parts.numel() + l_parts.numel() + o.numel() + lse.numel()) * 4
     r = dict(step_ms=ms_step, partials_ms=ms_part, partials_tflops=flops / ms_part / 1e9,
              merge_ms=ms_merge, merge_GBs=mbytes / ms_merge / 1e6, merge_bytes=mbytes,
+             merge_timing="back-to-back calls over 4 rotating input sets (608 MB > Infinity Cache)",
+             merge_single_flushed_ms=ms_merge_single,
+             merge_single_flushed_GBs=mbytes / ms_merge_single / 1e6,
              online_step_ms=ms_online, online_step_tflops=flops / ms_online / 1e9)
     log(f"[bench] workload {w.wid}: step {ms_step:.3f} ms, 8 partials {ms_part:.3f} ms "
-        f"({r['partials_tflops']:.1f} TFLOP/s), merge {ms_merge * 1e3:.1f} us ({r['merge_GBs']:.0f} GB/s); "
+        f"({r['partials_tflops']:.1f} TFLOP/s), merge {ms_merge * 1e3:.1f} us ({r['merge_GBs']:.0f} GB/s; "
+        f"single flushed call {ms_merge_single * 1e3:.1f} us, {r['merge_single_flushed_GBs']:.0f} GB/s); "
         f"step folding each block on arrival {ms_online:.3f} ms ({r['online_step_tflops']:.1f} TFLOP/s)")
+    if cpu_s > 0:
+        import numpy as np
+        import oracle
+        step()
+        torch.cuda.synchronize()
+
+        def run(n):
+            og = o[:, :n, :1].cpu().numpy()
+            lg = lse[:, :1, :n].cpu().numpy()
+            po, pl = [], []
+            for i in range(n_blk):
+                sl = slice(i * blk, (i + 1) * blk)
+                oi, li = oracle.attention_ref(q.values[:, :n, :1], k.values[:, sl, :1],
+                                              v.values[:, sl, :1], w.scale)
+                po.append(oi)
+                pl.append(li)
+            om, lm = oracle.merge_ref(np.stack(po), np.stack(pl))
+            return 4 * w.B * n * w.Skv * w.D, _errs(og, om, lg, lm)
+        r["cpu_baseline"] = oracle_leg(
+            run, 256, w.Sq, 256, cpu_s,
+            lambda n: f"query rows 0..{n - 1} of head 0: {n_blk} oracle partials over KV blocks of "
+                      f"{blk} keys, then the oracle merge, compared with the GPU's merged output",
+            r["partials_tflops"])
+        log_leg(w, r["cpu_baseline"])
     return r
 
 
@@ -225,12 +301,13 @@ def sparse_imbalance(I, w, mask, ws):
             "gpu_schedule_cu_makespan": sched["makespan_ratio"]}
 
 
-def bench_sparse(L, I, w, steps, warmup):
+def bench_sparse(L, I, w, steps, warmup, cpu_s=0.0):
     import torch
     log(f"[bench] workload {w.wid}: {w.name}: generating inputs")
     q, k, v = I.make_qkv(w, seed=0)
     qg, kg, vg = upload(q, w.dtype), upload(k, w.dtype), upload(v, w.dtype)
-    del q, k, v
+    if cpu_s <= 0:
+        del q, k, v
     nb = w.Sq // I.MASK_BLOCK
     mask, dens = I.make_block_mask(w.B, w.H, nb, nb, seed=0)
     mg = torch.from_numpy(mask).cuda()
@@ -249,12 +326,30 @@ def bench_sparse(L, I, w, steps, warmup):
         f"(mean density {r['density_mean']:.3f}); imbalance " +
         ", ".join(f"{k} {v:.3f}" for k, v in r["imbalance"].items()
                   if isinstance(v, float)))
+    if cpu_s > 0:
+        import oracle
+        mb = I.MASK_BLOCK
+
+        def run(n):
+            og = o[:, :n, :1].cpu().numpy()
+            lg = lse[:, :1, :n].cpu().numpy()
+            o_ref, l_ref = oracle.attention_ref(q.values[:, :n, :1], k.values[:, :, :1], v.values[:, :, :1],
+                                                w.scale, block_mask=mask[:, :1, :n // mb])
+            kept = int(mask[0, 0, :n // mb].astype(bool).sum())
+            return 4 * mb * mb * w.D * kept, _errs(og, o_ref, lg, l_ref)
+        r["cpu_baseline"] = oracle_leg(
+            run, mb * 2, w.Sq, mb, cpu_s,
+            lambda n: f"query rows 0..{n - 1} (mask rows 0..{n // mb - 1}) of head 0 against all "
+                      f"{w.Skv} keys under the mask; rate on the kept-block flops of the sample (the "
+                      "oracle masks a dense score matrix)",
+            r["tflops"])
+        log_leg(w, r["cpu_baseline"])
     return r
 
 
 # ---------------------------------------------------------------- CPU oracle
 
-def bench_bwd(L, I, w, steps, warmup):
+def bench_bwd(L, I, w, steps, warmup, cpu_s=0.0):
     """Backward of the dense forward: one step = one lsh_attn_bwd (row
     statistics, dK/dV and dQ kernels) on resident Q, K, V, dO, O, LSE.
     Algorithmic flops 10*B*H*Sq*Skv*D (dV, dP, dQ, dK: 2 each, plus the
@@ -265,7 +360,8 @@ def bench_bwd(L, I, w, steps, warmup):
     q, k, v = I.make_qkv(w, seed=0)
     do = I.make_dout(w, seed=0)
     qg, kg, vg, dog = (upload(x, w.dtype) for x in (q, k, v, do))
-    del q, k, v, do
+    if cpu_s <= 0:
+        del q, k, v, do
     o, lse = L.attn_fwd(qg, kg, vg)
     dq = torch.empty((w.B, w.Sq, w.H, w.D), dtype=torch.float32, device="cuda")
     dk = torch.empty((w.B, w.Skv, w.H, w.D), dtype=torch.float32, device="cuda")
@@ -281,7 +377,89 @@ def bench_bwd(L, I, w, steps, warmup):
     log(f"[bench] workload {w.wid}: {ms:.3f} ms/step, {r['tflops']:.1f} TFLOP/s algorithmic "
         f"({r['pct_of_bf16_peak']:.1f}% of the bf16 peak), {r['issued_matrix_tflops']:.1f} TFLOP/s "
         "of issued matrix work")
+    if cpu_s > 0:
+        import oracle
+
+        def run(n):
+            dqg = dq[:, :n, :1].cpu().numpy()
+            dq_ref, _, _ = oracle.attention_bwd_ref(q.values[:, :n, :1], k.values[:, :, :1], v.values[:, :, :1],
+                                                    do.values[:, :n, :1], w.scale)
+            return 10 * w.B * n * w.Skv * w.D, _errs(dqg, dq_ref, name="Q")
+        r["cpu_baseline"] = oracle_leg(
+            run, 128, w.Sq, 128, cpu_s,
+            lambda n: f"query rows 0..{n - 1} of head 0 through the whole oracle backward against all "
+                      f"{w.Skv} keys (S, dP, dV, dK, dQ products; dK and dV then sum over those rows "
+                      "only and are not compared), dQ compared",
+            r["tflops"])
+        log_leg(w, r["cpu_baseline"])
     return r
+
+
+def _blas_limit():
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=len(os.sched_getaffinity(0)), user_api="blas")
+    except Exception:   # pragma: no cover
+        import contextlib
+        return contextlib.nullcontext()
+
+
+def oracle_leg(run, n0, n_max, quantum, target_s, describe, gpu_tflops):
+    """Times the fp64 oracle on a sample of a workload on the host cores.
+
+    run(n) computes the oracle on a sample of size n (rows, heads, ...) and
+    returns (flops, errors), where flops counts the work the sample stands
+    for under the workload's own flop definition, and errors compares the
+    GPU's outputs on the sample with the oracle's. n starts at n0 and is
+    grown once (in multiples of quantum, at most n_max) so the timed run
+    takes about target_s seconds."""
+    def timed_run(n):
+        with _blas_limit():
+            t0 = time.perf_counter()
+            fl, err = run(n)
+            return time.perf_counter() - t0, fl, err
+    n = min(n0, n_max)
+    t, fl, err = timed_run(n)
+    if t < target_s and n < n_max:
+        n2 = int(min(n_max, n * target_s / max(t, 1e-3)) // quantum * quantum)
+        if n2 > n:
+            n = n2
+            t, fl, err = timed_run(n)
+    rate = fl / t / 1e12
+    return {"value": rate, "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle", "blas": blas_name(), "wall_s": round(t, 3),
+            "gflop": round(fl / 1e9, 3), "gflops_per_s": round(fl / t / 1e9, 2),
+            "sample": describe(n), "gpu_speedup": round(gpu_tflops / rate, 1),
+            "gpu_vs_oracle_on_sample": err}
+
+
+def _errs(o_gpu, o_ref, l_gpu=None, l_ref=None, name="O"):
+    import numpy as np
+    e = {f"max_abs_d{name}": float(np.abs(np.asarray(o_gpu, np.float64) - o_ref).max())}
+    if l_gpu is not None:
+        e["max_abs_dLSE"] = float(np.abs(np.asarray(l_gpu, np.float64) - l_ref).max())
+    return e
+
+
+def log_leg(w, leg):
+    log(f"[bench] workload {w.wid} oracle: {leg['sample']}: {leg['wall_s']:.2f} s on {leg['cores']} "
+        f"cores, {leg['gflops_per_s']:.1f} GFLOP/s fp64; GPU {leg['gpu_speedup']:.0f}x; "
+        + ", ".join(f"{k} {v:.2e}" for k, v in leg["gpu_vs_oracle_on_sample"].items()))
+
+
+def oracle_whole_small(I, w, q, k, v, o, lse, cpu_s, gpu_tflops):
+    """The fp32 workload is small enough for the oracle to do all of it."""
+    import oracle
+    og, lg = o.cpu().numpy(), lse.cpu().numpy()
+
+    def run(n):
+        heads = range(n)
+        o_ref, l_ref = oracle.attention_ref(q.values, k.values, v.values, w.scale, heads=heads)
+        return 4 * w.B * n * w.Sq * w.Skv * w.D, _errs(og[:, :, :n], o_ref[:, :, :n], lg[:, :n], l_ref[:, :n])
+    return oracle_leg(run, w.H, w.H, 1, cpu_s,
+                      lambda n: f"the whole workload ({w.B} x {n} heads x {w.Sq} queries x {w.Skv} keys), "
+                                "every output compared",
+                      gpu_tflops)
 
 
 def cpu_baseline(I, w, q, k, v, o_gpu, lse_gpu, target_s):
@@ -357,6 +535,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads", default="4,3,2,5,1,6",
                     help="comma list; 4 (the headline) is always run")
+    ap.add_argument("--cpu-seconds-each", type=float, default=4.0,
+                    help="seconds of fp64 oracle work on a sample of each secondary workload "
+                         "(skipped when --cpu-seconds is 0)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the CPU oracle sample (0 disables)")
     ap.add_argument("--hbm-copy-probe", action="store_true",
@@ -385,6 +566,7 @@ def main():
     if 4 not in wl:
         wl = [4] + wl
 
+    each_s = args.cpu_seconds_each if args.cpu_seconds > 0 else 0.0
     w4 = I.WORKLOADS[4]
     head, keep = bench_dense(L, I, w4, args.steps, args.warmup)
     secondary = {}
@@ -399,16 +581,20 @@ def main():
             continue
         w = I.WORKLOADS[wid]
         if wid == 3:
-            secondary[w.name] = bench_chunked(L, I, w, args.steps, args.warmup)
+            secondary[w.name] = bench_chunked(L, I, w, args.steps, args.warmup, each_s)
         elif wid == 2:
-            secondary[w.name] = bench_ring(L, I, w, args.steps, args.warmup)
+            secondary[w.name] = bench_ring(L, I, w, args.steps, args.warmup, each_s)
         elif wid == 5:
-            secondary[w.name] = bench_sparse(L, I, w, args.steps, args.warmup)
+            secondary[w.name] = bench_sparse(L, I, w, args.steps, args.warmup, each_s)
         elif wid == 1:
-            r, _ = bench_dense(L, I, w, args.steps, args.warmup)
+            r, keep = bench_dense(L, I, w, args.steps, args.warmup)
+            if each_s > 0:
+                r["cpu_baseline"] = oracle_whole_small(I, w, *keep, each_s, r["tflops"])
+                log_leg(w, r["cpu_baseline"])
+            del keep
             secondary[w.name] = r
         elif wid == 6:
-            secondary[w.name] = bench_bwd(L, I, w, args.steps, args.warmup)
+            secondary[w.name] = bench_bwd(L, I, w, args.steps, args.warmup, each_s)
         torch.cuda.empty_cache()
 
     ms = head["ms"]

@@ -1,4 +1,4 @@
-// Device helpers shared by the attention kernels (gfx950): vector types,
+// Device helpers shared by the kernels (gfx950): vector types,
 // LDS swizzles, the XCD-aware workgroup order, cross-half lane reductions,
 // wait/barrier helpers and the LDS-DMA load. Header-only; every helper is
 // inline and internal to the including translation unit.
@@ -31,8 +31,8 @@ __device__ __forceinline__ int swz_v(int row, int c) {
 }
 
 // Workgroups are handed to the 8 XCDs round-robin; remap so that each XCD
-// walks a contiguous range of (b, h, query-block) items and the K/V stream
-// of a head is shared inside one XCD's L2.
+// walks a contiguous range of work items (for attention, (b, h, query-block)
+// items, so the K/V stream of a head is shared inside one XCD's L2).
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
   constexpr int X = 8;
   const int per = n / X, rem = n % X;

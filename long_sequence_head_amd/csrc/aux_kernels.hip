@@ -2,15 +2,10 @@
 // that stands in for the Ulysses all-to-all, the log-sum-exp merge of
 // per-KV-block partial results, and the work order of the block-sparse
 // kernel.
-#include "lsh_internal.hpp"
+#include "attn_common.hpp"
 
 namespace lsh {
 namespace {
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kNegInf = -__builtin_inff();
 
 // ------------------------------------------------------------ head permute
 //
@@ -74,7 +69,11 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(
     const float* __restrict__ o_parts, const float* __restrict__ lse_parts, int n, int B, int Sq,
     int H, float* __restrict__ o, float* __restrict__ lse) {
   const unsigned rows = (unsigned)B * (unsigned)Sq * (unsigned)H;  // < 2^31
-  const unsigned row = blockIdx.x * (unsigned)(kMergeThreads / 32) + (threadIdx.x >> 5);
+  // XCD-aware block order: the blocks one XCD runs take consecutive rows,
+  // so that XCD's L2 serves each 64-byte line of the LSE arrays (16
+  // consecutive s of one h) to all the rows that use it
+  const unsigned row = (unsigned)xcd_remap((int)blockIdx.x, (int)gridDim.x) * (unsigned)(kMergeThreads / 32) +
+                       (threadIdx.x >> 5);
   const int l = threadIdx.x & 31;
   if (row >= rows) return;
   const unsigned bs = row / (unsigned)H;
