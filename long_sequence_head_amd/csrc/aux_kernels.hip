@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kPermThreads) void head_permute_kernel(
 // fold in with the running max: when a group raises M, what was summed so
 // far is scaled by exp(M_old - M_new). The sums run over k = 0, 1, ... in
 // order.
-constexpr int kMergeThreads = 256;
+constexpr int kMergeThreads = 128;
 constexpr int kMergeGroup = 8;
 
 __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(
