@@ -150,10 +150,11 @@ def test_rescale_paths_large_grid(L):
     offset: the running max moves on every tile, every other tile, every
     few tiles (with tile sums past the bound that skips the row max), or
     never after the first. H=64 and Sq=2048 give 512 workgroups of 256
-    rows, so the eight-wavefront kernel runs; an all-ones block mask runs
-    the block-sparse kernel. Both must equal, bit for bit, calls on 4 heads
-    at a time (the pipelined kernel, which takes the row max of every
-    tile); heads 0, 20, 40 and 60 are checked against the oracle."""
+    rows, so the 256-row kernel runs (two 16-query groups per wavefront);
+    an all-ones block mask runs the block-sparse kernel. Both must equal,
+    bit for bit, calls on 4 heads at a time (64 workgroups: the 128-row
+    kernel, one 16-query group per wavefront); heads 0, 20, 40 and 60 are
+    checked against the oracle."""
     G.announce("rescale paths, large grid")
     t = G.torch()
     B, Sq, Skv, H, D = 1, 2048, 1500, 64, 128
@@ -198,11 +199,11 @@ def test_run_to_run_bit_identical(L):
 
 
 def test_workgroup_size_does_not_change_bits(L):
-    """All 8 heads (512 workgroups of 256 rows: the eight-wavefront kernel)
-    vs head 0 alone (128 workgroups of 128 rows: the pipelined kernel) and a
-    {1, 7} chunking (its 1-head chunk on the pipelined kernel, its 7-head
-    chunk on the eight-wavefront one): neither the kernel, the grid size
-    nor the chunking may change a bit."""
+    """All 8 heads (512 workgroups of 256 rows: the 256-row kernel) vs head
+    0 alone (128 workgroups of 128 rows: the 128-row kernel) and a {1, 7}
+    chunking (its 1-head chunk on the 128-row kernel, its 7-head chunk on
+    the 256-row one): neither the kernel, the grid size nor the chunking may
+    change a bit."""
     G.announce("workgroup-size invariance")
     t = G.torch()
     S, H = 16384, 8
@@ -216,13 +217,13 @@ def test_workgroup_size_does_not_change_bits(L):
     assert t.equal(o1[:, :, :1], o3) and t.equal(l1[:, :1], l3)
 
 
-def test_eight_wave_kernel_strided(L):
+def test_large_grid_strided(L):
     """B=2, Sq=777 (last 256-row block holds 9 rows), Skv=333, H=64: 512
-    workgroups, so the eight-wavefront kernel runs, here on Q, K, V as views
-    of one packed [B, S, 3, H, D] buffer with O written into a wider one.
-    Four heads against the oracle on every row; every head bit-identical to
-    calls on 4 heads at a time (64-workgroup grids: the pipelined kernel)."""
-    G.announce("eight-wave kernel, strided")
+    workgroups, so the 256-row kernel runs, here on Q, K, V as views of one
+    packed [B, S, 3, H, D] buffer with O written into a wider one. Four
+    heads against the oracle on every row; every head bit-identical to
+    calls on 4 heads at a time (56-workgroup grids: the 128-row kernel)."""
+    G.announce("large grid, strided")
     t = G.torch()
     B, Sq, Skv, H, D = 2, 777, 333, 64, 128
     q, k, v = I.make_custom((B, Sq, H, D), (B, Skv, H, D), "bf16", seed=77)
@@ -242,7 +243,7 @@ def test_eight_wave_kernel_strided(L):
     sig = G.bf16_weight_sigma(oracle, q.values, k.values, v.values, 1 / math.sqrt(D), lse_ref,
                               heads=heads)
     og, lg = o.cpu().numpy(), lse.cpu().numpy()
-    G.check("eight-wave strided", "bf16", og[:, :, heads], lg[:, heads], o_ref[:, :, heads],
+    G.check("large grid strided", "bf16", og[:, :, heads], lg[:, heads], o_ref[:, :, heads],
             lse_ref[:, heads], sigma=sig[:, :, heads])
     assert t.isnan(wide[:, :, 0]).all() and t.isnan(wide[:, :, H + 1]).all(), "wrote outside O"
     assert not t.isnan(o).any() and not t.isnan(lse).any(), "unwritten output"
@@ -348,8 +349,8 @@ def test_partial_accumulate_small(L, dtype):
 
 
 def test_partial_accumulate_large_grid(L):
-    """H=32, Sq=4133: each fold is a 544-workgroup launch of the
-    eight-wavefront kernel. Three blocks (1500, 1500, 37 keys) against the
+    """H=32, Sq=4133: each fold is a 544-workgroup launch of the 256-row
+    kernel. Three blocks (1500, 1500, 37 keys) against the
     oracle on heads 0 and 31; the first fold bit-identical to
     lsh_attn_partial."""
     G.announce("partial accumulate, large grid")
@@ -453,7 +454,7 @@ def test_blocksparse_all_ones_equals_dense_bitwise(L, dtype):
 
 def test_blocksparse_all_ones_large_grid_equals_dense_bitwise(L):
     """H=32, S=4133: 1056 sparse workgroups, two to a CU, against the dense
-    call (544 workgroups of 256 rows: the eight-wavefront kernel); the last
+    call (544 workgroups of 256 rows: the 256-row kernel); the last
     key block holds 37 keys."""
     G.announce("sparse all-ones, large grid")
     t = G.torch()
