@@ -216,19 +216,25 @@ lsh_status lsh_head_permute(const void* src, void* dst, int32_t dtype,
  * workspace: at least lsh_attn_fwd_blocksparse_workspace(args) bytes; it
  * holds the launch schedule, readable after the call for diagnostics. With
  * n = B * H * ceil(Sq/128) items (item = (b * H + h) * ceil(Sq/128) + query
- * block), nk = ceil(Skv/128), R = n * 4 and T = B * H * 8, each rounded up
- * to 256 bytes:
- *   int32 counts[n]      at byte 0:         kept blocks of each item's mask row;
- *   int32 order[n]       at byte R:         item of each launch slot;
- *   int64 totals[B * H]  at byte 2 * R:     kept blocks of each head;
- *   uint16 kept[n][nk]   at byte 2 * R + T: each item's kept key blocks,
- *                                           ascending (counts[item] of them).
- * Heads go in descending total (ties: lower index first) and, inside a
- * head, items in descending count (ties: lower index first). Launch slots
- * are handed to the 8 XCDs in turn, so each XCD works through one head's
- * rows at a time (sharing its K/V in L2), every XCD gets an equal share of
- * each head, and the heaviest rows of a head start first. Same reuse rule
- * as the chunked workspace.
+ * block), G = B * H heads, nk = ceil(Skv/128), R = n * 4, T = G * 8 and
+ * K = n * nk * 2, each rounded up to 256 bytes:
+ *   int32 counts[n]      at byte 0:             kept blocks of each item's mask row;
+ *   int32 order[n]       at byte R:             item of each launch slot;
+ *   int64 totals[G]      at byte 2 * R:         kept blocks of each head;
+ *   uint16 kept[n][nk]   at byte 2 * R + T:     each item's kept key blocks,
+ *                                               ascending (counts[item] of them);
+ *   int32 place[G + 8]   at byte 2 * R + T + K: XCD placement of the heads.
+ * Launch slot s runs on XCD s mod 8. Heads are dealt to the 8 XCDs whole:
+ * in descending total (ties: lower index first), each to the XCD with the
+ * smallest total so far among those holding fewer than ceil(G / 8) heads
+ * (ties: lowest XCD); place[g] = x + 8 * k for the k-th head dealt to XCD x,
+ * place[G + x] = heads of XCD x. XCD x's list is its heads in the order
+ * dealt, each head's items in descending count (ties: lower index first);
+ * position j of that list (lists of L_x = place[G + x] * ceil(Sq/128)
+ * items) takes slot sum_x' min(L_x', j) + #{x' < x : L_x' > j}. So each
+ * head's K/V streams through one XCD's L2, one head at a time per XCD, and
+ * the heaviest rows of a head start first. Same reuse rule as the chunked
+ * workspace.
  */
 lsh_status lsh_attn_fwd_blocksparse(const lsh_attn_args* args,
                                     const uint8_t* block_mask,

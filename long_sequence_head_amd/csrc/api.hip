@@ -261,16 +261,18 @@ lsh_status blocksparse_launch(const lsh_attn_args* args, const uint8_t* block_ma
   p.n_mkb = (int32_t)n_mkb;
   const int32_t n_items = (int32_t)(args->B * args->H * n_mqb);
   // workspace: int32 counts[n_items] | int32 order[n_items] |
-  // int64 totals[B * H] | uint16 kept[n_items][n_mkb]
+  // int64 totals[B * H] | uint16 kept[n_items][n_mkb] | int32 place[B * H + 8]
   const size_t region = round_up((size_t)n_items * sizeof(int32_t), 256);
   const size_t tot_region = round_up((size_t)(args->B * args->H) * sizeof(long long), 256);
+  const size_t kept_region = round_up((size_t)n_items * (size_t)n_mkb * sizeof(unsigned short), 256);
   char* ws = static_cast<char*>(workspace);
   int32_t* counts = reinterpret_cast<int32_t*>(ws);
   int32_t* order = reinterpret_cast<int32_t*>(ws + region);
   long long* totals = reinterpret_cast<long long*>(ws + 2 * region);
   unsigned short* kept = reinterpret_cast<unsigned short*>(ws + 2 * region + tot_region);
+  int32_t* place = reinterpret_cast<int32_t*>(ws + 2 * region + tot_region + kept_region);
   hipError_t e = lsh::launch_sparse_schedule(block_mask, n_items, p.n_mkb, p.n_mqb, counts, totals,
-                                             order, kept, s);
+                                             order, kept, place, s);
   if (e != hipSuccess) return hip_status(e, fn);
   p.order = order;
   p.counts = counts;
@@ -522,7 +524,8 @@ size_t lsh_attn_fwd_blocksparse_workspace(const lsh_attn_args* args) {
   const int64_t n_mkb = (args->Skv + LSH_MASK_BLOCK - 1) / LSH_MASK_BLOCK;
   return 2 * round_up((size_t)n_items * sizeof(int32_t), 256) +
          round_up((size_t)(args->B * args->H) * sizeof(long long), 256) +
-         round_up((size_t)n_items * (size_t)n_mkb * sizeof(unsigned short), 256);
+         round_up((size_t)n_items * (size_t)n_mkb * sizeof(unsigned short), 256) +
+         round_up((size_t)(args->B * args->H + 8) * sizeof(int32_t), 256);
 }
 
 lsh_status lsh_attn_fwd_blocksparse(const lsh_attn_args* args, const uint8_t* block_mask,

@@ -164,12 +164,19 @@ __global__ __launch_bounds__(256) void sparse_count_kernel(const uint8_t* __rest
 }
 
 // Launch order of the block-sparse work items. Item i = g * per + r is
-// query block r of head g = b * H + h. Heads go in descending total kept
-// count (ties: lower head index first); inside a head, query blocks go in
-// descending kept count (ties: lower index first). Consecutive launch slots
-// go to the 8 XCDs in turn, so each XCD runs rows of one head at a time (its
-// 32 CUs share that head's K/V tiles in their L2) and every XCD gets an
-// equal share of every head; inside a head the heaviest rows start first.
+// query block r of head g = b * H + h. Launch slots go to the 8 XCDs in
+// turn (slot s runs on XCD s mod 8), so the order decides what each XCD's
+// L2 sees. Heads are dealt to the XCDs whole, by kept-block total: in
+// descending total (ties: lower head index first), each head goes to the
+// XCD with the smallest total so far among those holding fewer than
+// ceil(G / 8) heads (ties: lowest XCD), so every head's K/V is streamed
+// through one XCD's L2 and the XCDs carry about equal work. Each XCD's list
+// is its heads in the order dealt, each head's query blocks in descending
+// kept count (ties: lower index first): the XCD works through one head's
+// rows at a time, heaviest first. Position j of XCD x's list (lists of
+// L_x items) takes slot sum_x' min(L_x', j) + #{x' < x : L_x' > j}, i.e.
+// the lists interleave slot by slot (slot 8 j + x while all eight run).
+constexpr int kXcds = 8;
 
 // Kept-block total of each head: one wavefront per head (exact integer sum).
 __global__ __launch_bounds__(256) void sparse_total_kernel(const int* __restrict__ counts,
@@ -185,32 +192,59 @@ __global__ __launch_bounds__(256) void sparse_total_kernel(const int* __restrict
   if (lane == 0) totals[g] = t;
 }
 
-// order[per * rank(g) + rank_g(r)] = g * per + r, with
-//   rank(g)   = #{k : T_k > T_g} + #{k < g : T_k = T_g}            (T = totals)
+// Deals the heads to the XCDs (one workgroup): place[g] = x + 8 * k for
+// the k-th head dealt to XCD x, place[G + x] = heads of XCD x. The heads'
+// descending-total order goes through by_rank (G entries of scratch), with
+//   rank(g) = #{k : T_k > T_g} + #{k < g : T_k = T_g}.
+__global__ __launch_bounds__(256) void sparse_place_kernel(const long long* __restrict__ totals,
+                                                           int n_groups, int* __restrict__ by_rank,
+                                                           int* __restrict__ place) {
+  for (int g = threadIdx.x; g < n_groups; g += 256) {
+    const long long t_g = totals[g];
+    int rank = 0;
+    for (int k = 0; k < n_groups; ++k) {
+      const long long t_k = totals[k];
+      rank += (t_k > t_g) | ((t_k == t_g) & (k < g));
+    }
+    by_rank[rank] = g;
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  const int cap = (n_groups + kXcds - 1) / kXcds;
+  long long load[kXcds];
+  int cnt[kXcds];
+  for (int x = 0; x < kXcds; ++x) {
+    load[x] = 0;
+    cnt[x] = 0;
+  }
+  for (int r = 0; r < n_groups; ++r) {
+    const int g = by_rank[r];
+    int best = -1;
+    for (int x = 0; x < kXcds; ++x)
+      if (cnt[x] < cap && (best < 0 || load[x] < load[best])) best = x;
+    place[g] = best + kXcds * cnt[best];
+    ++cnt[best];
+    load[best] += totals[g];
+  }
+  for (int x = 0; x < kXcds; ++x) place[n_groups + x] = cnt[x];
+}
+
+// order[slot(g, r)] = g * per + r with j = per * k(g) + rank_g(r), where
 //   rank_g(r) = #{j : c_j > c_r} + #{j < r : c_j = c_r} over the head's
-//               query blocks (c = counts).
-// A workgroup ranks 256 query blocks of one head, reading the head's counts
-// from LDS in chunks (every lane reads the same entry: a broadcast).
+//               query blocks (c = counts),
+// and the slot of position j of XCD x(g) as above. A workgroup ranks 256
+// query blocks of one head, reading the head's counts from LDS in chunks
+// (every lane reads the same entry: a broadcast).
 constexpr int kOrderThreads = 256;
 constexpr int kOrderChunk = 4096;
 
 __global__ __launch_bounds__(kOrderThreads) void sparse_order_kernel(
-    const int* __restrict__ counts, const long long* __restrict__ totals, int n_groups, int per,
+    const int* __restrict__ counts, const int* __restrict__ place, int n_groups, int per,
     int* __restrict__ order) {
   __shared__ int cbuf[kOrderChunk];
-  __shared__ int grank;
   const int blocks_per_group = (per + kOrderThreads - 1) / kOrderThreads;
   const int g = blockIdx.x / blocks_per_group;
   const int r = (blockIdx.x % blocks_per_group) * kOrderThreads + threadIdx.x;
-  if (threadIdx.x == 0) grank = 0;
-  __syncthreads();
-  const long long t_g = totals[g];
-  int gr = 0;
-  for (int k = threadIdx.x; k < n_groups; k += kOrderThreads) {
-    const long long t_k = totals[k];
-    gr += (t_k > t_g) | ((t_k == t_g) & (k < g));
-  }
-  atomicAdd(&grank, gr);   // integer: the sum is exact in any order
   const int* c = counts + (int64_t)g * per;
   const int c_r = r < per ? c[r] : 0;
   int lr = 0;
@@ -224,8 +258,17 @@ __global__ __launch_bounds__(kOrderThreads) void sparse_order_kernel(
       lr += (c_j > c_r) | ((c_j == c_r) & (base + j < r));
     }
   }
-  __syncthreads();
-  if (r < per) order[(int64_t)grank * per + lr] = g * per + r;
+  if (r >= per) return;
+  const int pl = place[g];
+  const int x = pl % kXcds;
+  const long long j = (long long)per * (pl / kXcds) + lr;
+  long long slot = 0;
+  for (int x2 = 0; x2 < kXcds; ++x2) {
+    const long long len = (long long)per * place[n_groups + x2];
+    slot += len < j ? len : j;
+    if (x2 < x && len > j) ++slot;
+  }
+  order[slot] = g * per + r;
 }
 
 }  // namespace
@@ -255,7 +298,7 @@ hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, int32_
 
 hipError_t launch_sparse_schedule(const uint8_t* mask, int32_t n_items, int32_t n_mkb, int32_t per,
                                   int32_t* counts, long long* totals, int32_t* order,
-                                  unsigned short* kept, hipStream_t s) {
+                                  unsigned short* kept, int32_t* place, hipStream_t s) {
   hipLaunchKernelGGL(sparse_count_kernel, dim3((n_items + 3) / 4), dim3(256), 0, s, mask, n_items,
                      n_mkb, counts, kept);
   hipError_t e = hipGetLastError();
@@ -265,9 +308,14 @@ hipError_t launch_sparse_schedule(const uint8_t* mask, int32_t n_items, int32_t 
                      n_groups, per, totals);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // the order array is scratch for the heads' rank order until the order
+  // kernel overwrites it
+  hipLaunchKernelGGL(sparse_place_kernel, dim3(1), dim3(256), 0, s, totals, n_groups, order, place);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int blocks_per_group = (per + kOrderThreads - 1) / kOrderThreads;
   hipLaunchKernelGGL(sparse_order_kernel, dim3((unsigned)((int64_t)n_groups * blocks_per_group)),
-                     dim3(kOrderThreads), 0, s, counts, totals, n_groups, per, order);
+                     dim3(kOrderThreads), 0, s, counts, place, n_groups, per, order);
   return hipGetLastError();
 }
 

@@ -56,12 +56,12 @@ hipError_t launch_head_permute(const void* src, void* dst, int elem_bytes,
 hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, int32_t n,
                             int64_t B, int64_t Sq, int64_t H, float* o, float* lse,
                             hipStream_t s);
-// Kept-block counts and lists per item, totals per head and the launch
-// order of the block-sparse items (per = query blocks per head; n_items =
-// heads * per).
+// Kept-block counts and lists per item, totals per head, the heads' XCD
+// placement (heads + 8 entries) and the launch order of the block-sparse
+// items (per = query blocks per head; n_items = heads * per).
 hipError_t launch_sparse_schedule(const uint8_t* mask, int32_t n_items, int32_t n_mkb, int32_t per,
                                   int32_t* counts, long long* totals, int32_t* order,
-                                  unsigned short* kept, hipStream_t s);
+                                  unsigned short* kept, int32_t* place, hipStream_t s);
 
 // Query rows per tile of the backward's per-row workspace (and of the
 // dK/dV kernel's query loop).

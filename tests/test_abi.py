@@ -190,9 +190,10 @@ def test_blocksparse_validation():
     a = _valid_args(Sq=300, Skv=257, H=4)
     need = lib.lsh_attn_fwd_blocksparse_workspace(ctypes.byref(a))
     # counts and order (int32 per item), totals (int64 per head), kept lists
-    # (uint16 per item and key block), each rounded up to 256 bytes
+    # (uint16 per item and key block), XCD placement (int32 per head + 8),
+    # each rounded up to 256 bytes
     assert need == 2 * ((4 * 3 * 4 + 255) // 256 * 256) + (4 * 8 + 255) // 256 * 256 + \
-        (4 * 3 * 3 * 2 + 255) // 256 * 256
+        (4 * 3 * 3 * 2 + 255) // 256 * 256 + ((4 + 8) * 4 + 255) // 256 * 256
     m = 1 << 22
     assert lib.lsh_attn_fwd_blocksparse(ctypes.byref(a), None, m, need, None) == _lib.LSH_ERR_INVALID
     assert lib.lsh_attn_fwd_blocksparse(ctypes.byref(a), m, m, need - 1, None) == _lib.LSH_ERR_WORKSPACE

@@ -483,14 +483,26 @@ def test_blocksparse_diagonal_is_blockwise_dense(L):
 
 
 def _expected_schedule(mask):
-    """The launch schedule lsh.h documents, computed from the mask."""
+    """The launch schedule lsh.h documents, computed from the mask: heads
+    dealt whole to the 8 XCDs by kept-block total, each XCD's list (its
+    heads in the order dealt, each head's rows heaviest first) interleaved
+    slot by slot."""
     B, H, nq, _ = mask.shape
+    G = B * H
     counts = (mask != 0).sum(axis=-1).reshape(-1).astype(np.int64)
-    totals = counts.reshape(B * H, nq).sum(axis=1)
-    heads = sorted(range(B * H), key=lambda g: (-totals[g], g))
-    order = []
+    totals = counts.reshape(G, nq).sum(axis=1)
+    heads = sorted(range(G), key=lambda g: (-totals[g], g))
+    cap = -(-G // 8)
+    load, xcd_heads = [0] * 8, [[] for _ in range(8)]
     for g in heads:
-        order += [g * nq + r for r in sorted(range(nq), key=lambda r: (-counts[g * nq + r], r))]
+        x = min((x for x in range(8) if len(xcd_heads[x]) < cap), key=lambda x: (load[x], x))
+        xcd_heads[x].append(g)
+        load[x] += int(totals[g])
+    lists = [[g * nq + r for g in hs for r in sorted(range(nq), key=lambda r: (-counts[g * nq + r], r))]
+             for hs in xcd_heads]
+    order = []
+    for j in range(max(len(lst) for lst in lists)):
+        order += [lst[j] for lst in lists if j < len(lst)]
     return counts, totals, np.array(order, dtype=np.int64)
 
 
