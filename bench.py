@@ -302,6 +302,7 @@ def sparse_imbalance(I, w, mask, ws):
 
 
 def bench_sparse(L, I, w, steps, warmup, cpu_s=0.0):
+    import numpy as np
     import torch
     log(f"[bench] workload {w.wid}: {w.name}: generating inputs")
     q, k, v = I.make_qkv(w, seed=0)
@@ -321,6 +322,7 @@ def bench_sparse(L, I, w, steps, warmup, cpu_s=0.0):
     r = dict(ms=ms, tflops=flops / ms / 1e9, kept_blocks=nnz, kept_flops=flops,
              density_mean=float(dens.mean()), density_min=float(dens.min()),
              density_max=float(dens.max()),
+             density_per_head=[round(float(x), 4) for x in np.asarray(dens).ravel()],
              imbalance=sparse_imbalance(I, w, mask, ws))
     log(f"[bench] workload {w.wid}: {ms:.3f} ms, {r['tflops']:.1f} TFLOP/s on kept blocks "
         f"(mean density {r['density_mean']:.3f}); imbalance " +
