@@ -116,13 +116,19 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
   constexpr int LPW = (kTileBytes / 1024) / WAVES;   // 1-KiB loads per wavefront per tile
   constexpr int PF = 2;                                // fragment reads ahead, in slots
   constexpr int kSlotBytes = kTileBytes;
+  // An LDS read adds at most 65535 to its address register. The V slots sit
+  // first and the K slots after them; with three slots per ring the K slots
+  // reach 96 KiB, so the K read bases carry 32 KiB in the register and every
+  // fragment read takes its slot and half-tile as an immediate offset (no
+  // address arithmetic in the key loop).
+  constexpr int kKBias = 2 * S * kSlotBytes > 65536 ? 32768 : 0;
   static_assert(LPW * WAVES * 1024 == kTileBytes, "tile/threads mismatch");
   static_assert(S == 2 || S == 3, "2 or 3 slots per ring");
   static_assert(!SPARSE || BM == kMaskBlock, "a sparse workgroup covers one mask row");
   static_assert(QG == 1 || QG == 2, "one or two 16-query groups per wavefront");
   static_assert(WAVES * (8192 + 128) <= 2 * S * kSlotBytes, "epilogue staging must fit the tile slots");
 
-  // K slots 0..S-1, then V slots 0..S-1
+  // V slots 0..S-1, then K slots 0..S-1
   __shared__ __attribute__((aligned(1024))) unsigned char lds_buf[2 * S * kSlotBytes];
   extern __shared__ unsigned short kept_dyn[];
 
@@ -184,13 +190,13 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
   const uint32_t lds0 = lds_addr(lds_buf);
   auto issue_k = [&](int t) __device__ {
     const uint32_t base = (uint32_t)key0_of(t) * k_rb;
-    const uint32_t dst = lds0 + (t % S) * kSlotBytes + wave * LPW * 1024;
+    const uint32_t dst = lds0 + (S + t % S) * kSlotBytes + wave * LPW * 1024;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) lds_dma16(dst + j * 1024, koff[j] + base, k_rsrc);
   };
   auto issue_v = [&](int t) __device__ {
     const uint32_t base = (uint32_t)key0_of(t) * v_rb;
-    const uint32_t dst = lds0 + (S + t % S) * kSlotBytes + wave * LPW * 1024;
+    const uint32_t dst = lds0 + (t % S) * kSlotBytes + wave * LPW * 1024;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) lds_dma16(dst + j * 1024, voff[j] + base, v_rsrc);
   };
@@ -228,7 +234,10 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
   // 4 dc + g, stored at chunk (4 dc + g) ^ t.
   uint32_t kofs[4];
 #pragma unroll
-  for (int dc = 0; dc < 4; ++dc) kofs[dc] = (uint32_t)(t16 * 256 + (((4 * dc + g) ^ t16) << 4));
+  for (int dc = 0; dc < 4; ++dc) {
+    kofs[dc] = (uint32_t)(t16 * 256 + (((4 * dc + g) ^ t16) << 4)) + (uint32_t)kKBias;
+    asm volatile("" : "+v"(kofs[dc]));   // keep the bias in the register
+  }
   // V^T fragment (16 head_dim x 32 keys: A operand) of head_dim group dg:
   // lane (g, t) receives column 16 dg + t of unit rows 4 g .. 4 g + 3, then
   // of rows 16 + 4 g .. +3; for that it points at row 4 g + t / 4 (+16),
@@ -239,12 +248,13 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
 #pragma unroll
   for (int dg = 0; dg < 8; ++dg) vofs[dg] = vbase + 32u * (uint32_t)(dg ^ (vr & 7));
   auto kread = [&](int slot, int uh, int kg, int dc) __device__ -> bf16x8 {
-    const LDS_AS unsigned char* b = (LDS_AS const unsigned char*)lds_buf + slot * kSlotBytes;
+    const LDS_AS unsigned char* b =
+        (LDS_AS const unsigned char*)lds_buf + (S + slot) * kSlotBytes - kKBias;
     return *(LDS_AS const bf16x8*)(b + kofs[dc] + uh * 8192 + kg * 4096);
   };
   auto vread = [&](int slot, int uh, int dg) __device__ -> bf16x8 {
     const LDS_AS unsigned char* b =
-        (LDS_AS const unsigned char*)lds_buf + (S + slot) * kSlotBytes + uh * 8192 + vofs[dg];
+        (LDS_AS const unsigned char*)lds_buf + slot * kSlotBytes + uh * 8192 + vofs[dg];
     const s16x4 w0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)b);
     const s16x4 w1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(b + 4096));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7));
