@@ -25,6 +25,9 @@ SHAPES = [  # (B, Sq, Skv, H)
     (1, 1, 1, 1), (1, 2, 3, 2), (1, 63, 64, 1), (1, 64, 65, 2), (2, 127, 128, 2),
     (1, 128, 129, 3), (1, 200, 255, 2), (1, 257, 256, 2), (2, 300, 1000, 3),
     (1, 1000, 1000, 4), (1, 513, 77, 2),
+    # short query ranges against long key ranges, odd and even tile counts,
+    # last tiles of one key
+    (1, 1, 1024, 1), (1, 129, 1025, 2), (2, 300, 1100, 3), (1, 1000, 1500, 2), (1, 64, 4097, 2),
 ]
 
 
@@ -185,6 +188,32 @@ def test_rescale_paths_large_grid(L):
     og, lg = o.cpu().numpy(), lse.cpu().numpy()
     G.check("rescale paths", "bf16", og[:, :, heads], lg[:, heads], o_ref[:, :, heads],
             lse_ref[:, heads], sigma=sig[:, :, heads])
+
+
+def test_odd_tile_count_bitwise(L):
+    """Sq = Skv = 1025 (17 key tiles, the last holding one key; the last
+    query block one row). Against the oracle on every row; an all-ones block
+    mask, a {1, 2} head chunking and each batch entry on its own give the
+    same bits."""
+    G.announce("odd tile count")
+    t = G.torch()
+    B, Sq, Skv, H = 2, 1025, 1025, 3
+    q, k, v = I.make_custom((B, Sq, H, 128), (B, Skv, H, 128), "bf16", seed=97)
+    qg, kg, vg = G.to_gpu(q, "bf16"), G.to_gpu(k, "bf16"), G.to_gpu(v, "bf16")
+    o, lse = G.poisoned_outputs(B, Sq, H)
+    L.attn_fwd(qg, kg, vg, o=o, lse=lse)
+    o_ref, lse_ref = oracle.attention_ref(q.values, k.values, v.values, 1 / math.sqrt(128))
+    sig = G.bf16_weight_sigma(oracle, q.values, k.values, v.values, 1 / math.sqrt(128), lse_ref)
+    G.check("odd tile count", "bf16", o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, sigma=sig)
+    ones = t.ones((B, H, -(-Sq // 128), -(-Skv // 128)), dtype=t.uint8, device="cuda")
+    o2, l2 = L.attn_fwd_blocksparse(qg, kg, vg, ones)
+    assert t.equal(o, o2) and t.equal(lse, l2), "block-sparse all-ones differs"
+    o3, l3 = L.attn_fwd_chunked(qg, kg, vg, [1, 2])
+    t.cuda.synchronize()
+    assert t.equal(o, o3) and t.equal(lse, l3), "chunked differs"
+    for b in range(B):
+        o4, l4 = L.attn_fwd(qg[b:b + 1], kg[b:b + 1], vg[b:b + 1])
+        assert t.equal(o[b:b + 1], o4) and t.equal(lse[b:b + 1], l4), f"batch entry {b}"
 
 
 def test_run_to_run_bit_identical(L):
@@ -408,6 +437,9 @@ SPARSE_CASES = [  # (Sq, Skv, H, B)
     (256, 320, 2, 1), (256, 321, 2, 1),
     # two batch entries with different masks
     (700, 900, 3, 2),
+    # last key block of 65 keys (its second half holds one), and of exactly
+    # 64 (second half empty), over many blocks
+    (700, 1089, 2, 2), (1000, 1344, 1, 1),
 ]
 
 
