@@ -95,15 +95,15 @@ __device__ __forceinline__ void mfma_drain() {
 // tile). Unit u has three parts: A(u), the 16 MFMAs of S and dP; E(u), the
 // elementwise work that turns them into P and dS (bf16, packed as the B
 // operands of the next products); B(u), the 16 MFMAs of dV^T += dO^T P and
-// dK^T += Q^T dS. The loop runs A(u) alone, then B(u-1) interleaved with
-// E(u): the elementwise work of one unit hides under the gradient products
-// of the previous one, and only one unit's S and dP are live at a time
-// (P and dS are double-buffered instead). Fragments are read from LDS two
-// MFMAs ahead of their use.
+// dK^T += Q^T dS. Each phase of the loop issues A(u+1) and B(u-1) on
+// alternate MFMA slots with E(u) spread over them, so the elementwise work
+// of one unit hides under 32 MFMAs of its neighbours; S and dP of two units
+// are live (A writes the one E is not reading), P and dS are double-buffered
+// too.
 //
-// Step t covers units 2t and 2t+1 of tile t: A(2t+1), B(2t) | E(2t+1), then
-// (once tile t+1 has landed and every wavefront has passed the barrier)
-// A(2t+2), B(2t+1) | E(2t+2). After that barrier no wavefront reads tile
+// Step t covers units 2t+1 and 2t+2: once tile t+1 has landed and every
+// wavefront has passed the barrier, A(2t+2) | B(2t) | E(2t+1), then
+// A(2t+3) | B(2t+1) | E(2t+2). After that barrier no wavefront reads tile
 // t-1 again, so the loads of tile t+2 go into its slot; each tile has about
 // one step to land.
 __global__ __launch_bounds__(kBwdWaves * 64, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
@@ -204,94 +204,99 @@ __global__ __launch_bounds__(kBwdWaves * 64, 1) void attn_bwd_dkdv_kernel(BwdPar
     acc_dk[db] = f32x16{};
   }
   mfma_drain();
-  f32x16 sS, sD;            // S and dP of the unit in flight:
+  f32x16 sS[2], sD[2];      // S and dP of two consecutive units (by unit parity):
                             // register r <-> query 32 qb + 8 (r / 4) + 4 hh + r % 4
-  bf16x8 pp[2][2], pds[2][2];   // P and dS of two consecutive units, as B operands
+  bf16x8 pp[2][2], pds[2][2];   // P and dS of two consecutive units (by unit parity),
+                                // as B operands
 
-  // A(unit qa of tiles tq/td): S and dP into sS, sD
-  auto phase_a = [&](const unsigned char* tq, const unsigned char* td, int qa) __device__ {
-    bf16x8 fq[8], fd[8];
-    fq[0] = rowread(tq, qa, 0);
-    fd[0] = rowread(td, qa, 0);
-    fq[1] = rowread(tq, qa, 1);
-    fd[1] = rowread(td, qa, 1);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int k = i >> 1;
-      if ((i & 1) == 0) {
-        if (k + 2 < 8) fq[k + 2] = rowread(tq, qa, k + 2);
-        sS = mfma16(fq[k], kf[k], k == 0 ? f32x16{} : sS);
-      } else {
-        if (k + 2 < 8) fd[k + 2] = rowread(td, qa, k + 2);
-        sD = mfma16(fd[k], vf[k], k == 0 ? f32x16{} : sD);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // B(unit qb of tiles tq/td, P and dS from set sb): dV^T += dO^T P,
-  // dK^T += Q^T dS, interleaved (if DO_E) with E of the unit in sS/sD
-  // (block qe of aux tile ta) into set se.
-  auto phase_be = [&](const bool DO_B, const unsigned char* tq, const unsigned char* td, int qb,
-                      int sb, const bool DO_E, const unsigned char* ta, int qe, int se) __device__ {
-    auto frag = [&](int m) __device__ -> bf16x8 {
-      const int i = (qb * 2 + (m >> 3)) * 4 + ((m >> 1) & 3);
-      return tr_read((m & 1) ? tq : td, tofs, i);
+  // One phase of 32 MFMA slots:
+  //  * A (if DO_A): S and dP of the unit in block qa of tiles tqa/tda, into
+  //    set na, on the even slots (S and dP alternating over head_dim chunks);
+  //  * B (if DO_B): dV^T += dO^T P and dK^T += Q^T dS of the unit in block qb
+  //    of tiles tqb/tdb, with P and dS of set nb, on the odd slots;
+  //  * E (if DO_E): the elementwise step of the unit in set ne (block qe of
+  //    aux tile ta) into P and dS set ne, one value beside each odd slot.
+  // Fragments are read one MFMA of their product (two slots) ahead: two
+  // ahead, with both units' S and dP live, the kernel spills.
+  auto phase = [&](const bool DO_A, const unsigned char* tqa, const unsigned char* tda, int qa,
+                   int na, const bool DO_B, const unsigned char* tqb, const unsigned char* tdb,
+                   int qb, int nb, const bool DO_E, const unsigned char* ta, int qe,
+                   int ne) __device__ {
+    // A MFMA j: head_dim fragment j / 2 of Q (even j, S) or dO (odd j, dP)
+    auto afrag = [&](int j) __device__ -> bf16x8 {
+      return rowread((j & 1) ? tda : tqa, qa, j >> 1);
     };
-    bf16x8 f[16];
+    // B MFMA m: transposed fragment of dO (even m, into dV) or Q (odd m, into dK)
+    auto bfrag = [&](int m) __device__ -> bf16x8 {
+      const int i = (qb * 2 + (m >> 3)) * 4 + ((m >> 1) & 3);
+      return tr_read((m & 1) ? tqb : tdb, tofs, i);
+    };
+    bf16x8 fa[16], fb[16];
     f32x4 l4[4], d4[4];
-    if (DO_B) {
-      f[0] = frag(0);
-      f[1] = frag(1);
+#pragma unroll
+    for (int j = 0; j < 1; ++j) {
+      if (DO_A) fa[j] = afrag(j);
+      if (DO_B) fb[j] = bfrag(j);
     }
     if (DO_E) {
       l4[0] = auxread(ta, true, qe, 0);
       d4[0] = auxread(ta, false, qe, 0);
     }
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      if (DO_B) {
-        if (m + 2 < 16) f[m + 2] = frag(m + 2);
-        const int jj = m >> 3, db = (m >> 1) & 3;
-        if (m & 1)
-          mfma_acc_agpr(acc_dk[db], f[m], pds[sb][jj]);
-        else
-          mfma_acc_agpr(acc_dv[db], f[m], pp[sb][jj]);
-      }
-      if (DO_E) {
-        const int r = m, g = r >> 2, e = r & 3;
-        if (e == 0 && g + 1 < 4) {
-          l4[g + 1] = auxread(ta, true, qe, g + 1);
-          d4[g + 1] = auxread(ta, false, qe, g + 1);
+    for (int s = 0; s < 32; ++s) {
+      const int u = s >> 1;   // index of the MFMA within its product
+      if ((s & 1) == 0) {
+        if (DO_A) {
+          if (u + 1 < 16) fa[u + 1] = afrag(u + 1);
+          const int k = u >> 1;
+          if ((u & 1) == 0)
+            sS[na] = mfma16(fa[u], kf[k], k == 0 ? f32x16{} : sS[na]);
+          else
+            sD[na] = mfma16(fa[u], vf[k], k == 0 ? f32x16{} : sD[na]);
         }
-        const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sS[r], c, -l4[g][e]));
-        asm volatile("" ::"v"(x));   // computed here, next to this MFMA
-        const float y = x * (sD[r] - d4[g][e]);
-        pp[se][r >> 3][r & 7] = (__bf16)x;
-        pds[se][r >> 3][r & 7] = (__bf16)y;
+      } else {
+        if (DO_B) {
+          if (u + 1 < 16) fb[u + 1] = bfrag(u + 1);
+          const int jj = u >> 3, db = (u >> 1) & 3;
+          if (u & 1)
+            mfma_acc_agpr(acc_dk[db], fb[u], pds[nb][jj]);
+          else
+            mfma_acc_agpr(acc_dv[db], fb[u], pp[nb][jj]);
+        }
+        if (DO_E) {
+          const int r = u, g = r >> 2, e = r & 3;
+          if (e == 0 && g + 1 < 4) {
+            l4[g + 1] = auxread(ta, true, qe, g + 1);
+            d4[g + 1] = auxread(ta, false, qe, g + 1);
+          }
+          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(sS[ne][r], c, -l4[g][e]));
+          asm volatile("" ::"v"(x));   // computed here, next to this MFMA
+          const float y = x * (sD[ne][r] - d4[g][e]);
+          pp[ne][r >> 3][r & 7] = (__bf16)x;
+          pds[ne][r >> 3][r & 7] = (__bf16)y;
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   const int n_t = p.n_qt;
-  // step t: units 2t (P, dS in set 0) and 2t+1 (set 1) of tile t
+  // Step t covers units 2t+1 and 2t+2: after tile t+1 has landed and every
+  // wavefront has passed the barrier (so no one still reads tile t-1, whose
+  // slot takes tile t+2), phase 1 is A(2t+2) | B(2t) | E(2t+1) and phase 2
+  // A(2t+3) | B(2t+1) | E(2t+2). Units of even index use set 0, odd set 1.
   auto step = [&](int s, int t, const bool HAS_NEXT) __device__ {
     const unsigned char* tq = qslot(s);
     const unsigned char* td = dslot(s);
     const unsigned char* ta = aslot(s);
     const int s1 = (s + 1) % 3;
-    phase_a(tq, td, 1);
-    phase_be(true, tq, td, 0, 0, true, ta, 1, 1);
     if (HAS_NEXT) {
       wait_vmcnt<0>();   // tile t+1 (the only loads in flight)
       barrier_no_fence();
       if (t + 2 < n_t) issue(t + 2, (s + 2) % 3);
-      phase_a(qslot(s1), dslot(s1), 0);
-      phase_be(true, tq, td, 1, 1, true, aslot(s1), 0, 0);
-    } else {
-      phase_be(true, tq, td, 1, 1, false, ta, 0, 0);
     }
+    phase(HAS_NEXT, qslot(s1), dslot(s1), 0, 0, true, tq, td, 0, 0, true, ta, 1, 1);
+    phase(HAS_NEXT, qslot(s1), dslot(s1), 1, 1, true, tq, td, 1, 1, HAS_NEXT, aslot(s1), 0, 0);
   };
 
   issue(0, 0);
@@ -302,8 +307,9 @@ __global__ __launch_bounds__(kBwdWaves * 64, 1) void attn_bwd_dkdv_kernel(BwdPar
     wait_vmcnt<0>();
   }
   barrier_no_fence();
-  phase_a(lq0, ld0, 0);
-  phase_be(false, lq0, ld0, 0, 0, true, la0, 0, 0);
+  // A(0) alone, then A(1) | E(0)
+  phase(true, lq0, ld0, 0, 0, false, lq0, ld0, 0, 0, false, la0, 0, 0);
+  phase(true, lq0, ld0, 1, 1, false, lq0, ld0, 0, 0, true, la0, 0, 0);
   // t is a multiple of 3 at the top of the loop, so every slot index is a
   // compile-time constant.
   int t = 0;
