@@ -194,10 +194,10 @@ def bench_ring(L, I, w, steps, warmup, cpu_s=0.0):
     l_run = torch.empty_like(lse)
 
     def step_online():
-        # each block folded into the running result as it arrives
-        o_run.zero_()
-        l_run.fill_(float("-inf"))
-        for i in range(n):
+        # each block folded into the running result as it arrives; the first
+        # one starts it (folding it into O = 0, LSE = -inf gives the same bits)
+        L.attn_partial(qg, kb[0], vb[0], o=o_run, lse=l_run)
+        for i in range(1, n):
             L.attn_partial_accumulate(qg, kb[i], vb[i], o_run, l_run)
     ms_step, _ = timed(step, steps, warmup)
     ms_part, _ = timed(partials, steps, warmup)
