@@ -620,7 +620,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_entry(ms),
-                     "kernel": "attn_fwd_bf16_p8_kernel",
+                     "kernel": "attn_fwd_bf16_p8t_kernel",
                      "algorithmic_flops_per_launch": head["flops"]},
         "cpu_baseline": cpu,
         "workloads": secondary,

@@ -109,8 +109,16 @@ __device__ __forceinline__ int tile_key0(int t, const unsigned short* kept) {
 // wavefront) then hit every LDS bank once.
 __device__ __forceinline__ int swz_v16(int row, int c) { return c ^ (2 * (row & 7)); }
 
+// LDS of one instance: V slots 0..S-1, then K slots 0..S-1.
+template <int S>
+constexpr int ring_bytes() { return 2 * S * kTileBytes; }
+
+// One workgroup's work: query rows row0 .. row0 + BM - 1 of the (b, h) of
+// work item `item` (whose mask row, when SPARSE, lists the kept key
+// blocks), with lds_buf the workgroup's ring_bytes<S>() of LDS.
 template <int WAVES, int QG, int S, bool SPARSE>
-__device__ __forceinline__ void attention16(const AttnParams& p) {
+__device__ __forceinline__ void attention16(const AttnParams& p, unsigned char* lds_buf, int item,
+                                            int row0) {
   constexpr int RW = 16 * QG;                          // query rows per wavefront
   constexpr int BM = WAVES * RW;
   constexpr int LPW = (kTileBytes / 1024) / WAVES;   // 1-KiB loads per wavefront per tile
@@ -126,23 +134,16 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
   static_assert(S == 2 || S == 3, "2 or 3 slots per ring");
   static_assert(!SPARSE || BM == kMaskBlock, "a sparse workgroup covers one mask row");
   static_assert(QG == 1 || QG == 2, "one or two 16-query groups per wavefront");
-  static_assert(WAVES * (8192 + 128) <= 2 * S * kSlotBytes, "epilogue staging must fit the tile slots");
+  static_assert(WAVES * (8192 + 128) <= ring_bytes<S>(), "epilogue staging must fit the tile slots");
+  static_assert(ring_bytes<S>() == 2 * S * kSlotBytes, "LDS layout");
 
-  // V slots 0..S-1, then K slots 0..S-1
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_buf[2 * S * kSlotBytes];
   extern __shared__ unsigned short kept_dyn[];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t16 = lane & 15, g = lane >> 4;
-  int item;
-  if constexpr (SPARSE) {
-    item = p.order ? p.order[blockIdx.x] : (int)blockIdx.x;
-  } else {
-    item = xcd_remap(blockIdx.x, gridDim.x);
-  }
   const Item it = decode_item(item, p.n_qblk, p.H);
-  const int q0 = it.qblk * BM + wave * RW;    // first query row of the wavefront
+  const int q0 = row0 + wave * RW;    // first query row of the wavefront
   const __bf16* qp = static_cast<const __bf16*>(p.q) + it.b * p.q_sb + it.h * p.q_sh;
   const __bf16* kp = static_cast<const __bf16*>(p.k) + it.b * p.k_sb + it.h * p.k_sh;
   const __bf16* vp = static_cast<const __bf16*>(p.v) + it.b * p.v_sb + it.h * p.v_sh;
@@ -616,11 +617,13 @@ __device__ __forceinline__ void attention16(const AttnParams& p) {
   }
 }
 
-// The three bf16 kernels, one template (same per-query arithmetic, so the
-// same bits):
+// The bf16 kernels, one template (same per-query arithmetic, so the same
+// bits):
 //  * dense, large grids: 8 wavefronts of 32 query rows (256 rows), one
 //    workgroup per CU, two wavefronts per SIMD, three slots per ring
-//    (96 KiB);
+//    (96 KiB); where each XCD's last round would hold only a few of these
+//    workgroups, those items run as two 128-row halves each instead (the
+//    next kernel's shape) in the same launch;
 //  * dense grids that 256-row workgroups would leave partly idle where
 //    128-row ones would not (a ring round of 4096 queries x 8 heads): 8
 //    wavefronts of 16 rows (128 rows), still two wavefronts per SIMD; each
@@ -634,16 +637,48 @@ constexpr int kH8Waves = 8;
 constexpr int kH8BM = kH8Waves * 16;
 constexpr int kS4Waves = 4;
 
+constexpr int kXcdCount = 8;
+
 __global__ __launch_bounds__(kP8Waves * 64, 1) void attn_fwd_bf16_p8_kernel(AttnParams p) {
-  attention16<kP8Waves, 2, 3, false>(p);
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[ring_bytes<3>()];
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  attention16<kP8Waves, 2, 3, false>(p, lds, item, decode_item(item, p.n_qblk, p.H).qblk * kP8BM);
+}
+
+// 256-row items, the last p.n_tail of each XCD's range split in halves.
+// XCD x owns items x * per .. x * per + per - 1 (per = p.n_items / 8) and
+// runs blocks 8 k + x, k = 0 .. per + n_tail - 1: block k runs item
+// x * per + k whole while k < per - n_tail, and after that the halves of
+// the remaining items in turn (rows 0..127, then 128..255 of each; a half
+// that starts past Sq has nothing to do).
+__global__ __launch_bounds__(kP8Waves * 64, 1) void attn_fwd_bf16_p8t_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[ring_bytes<3>()];
+  const int x = (int)blockIdx.x % kXcdCount, k = (int)blockIdx.x / kXcdCount;
+  const int per = p.n_items / kXcdCount;
+  const int whole = per - p.n_tail;
+  if (k < whole) {
+    const int item = x * per + k;
+    attention16<kP8Waves, 2, 3, false>(p, lds, item, decode_item(item, p.n_qblk, p.H).qblk * kP8BM);
+  } else {
+    const int j = k - whole;
+    const int item = x * per + whole + (j >> 1);
+    const int row0 = decode_item(item, p.n_qblk, p.H).qblk * kP8BM + (j & 1) * kH8BM;
+    if (row0 >= p.Sq) return;   // the second half of a last block of at most 128 rows
+    attention16<kH8Waves, 1, 3, false>(p, lds, item, row0);
+  }
 }
 
 __global__ __launch_bounds__(kH8Waves * 64, 1) void attn_fwd_bf16_h8_kernel(AttnParams p) {
-  attention16<kH8Waves, 1, 3, false>(p);
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[ring_bytes<3>()];
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  attention16<kH8Waves, 1, 3, false>(p, lds, item, decode_item(item, p.n_qblk, p.H).qblk * kH8BM);
 }
 
 __global__ __launch_bounds__(kS4Waves * 64, 2) void attn_fwd_bf16_s4_kernel(AttnParams p) {
-  attention16<kS4Waves, 2, 2, true>(p);
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[ring_bytes<2>()];
+  const int item = p.order ? p.order[blockIdx.x] : (int)blockIdx.x;
+  attention16<kS4Waves, 2, 2, true>(p, lds, item,
+                                    decode_item(item, p.n_qblk, p.H).qblk * kMaskBlock);
 }
 
 // ------------------------------------------------------------------ f32 path
@@ -975,12 +1010,22 @@ hipError_t launch_attn_dense(const AttnParams& p0, DType dt, hipStream_t s) {
   }
   // 256-row workgroups unless their grid would leave CUs idle where the
   // 128-row one would not (a ring round of 4096 queries x 8 heads: 128
-  // workgroups of 256 rows against 256 of 128). Both give the same bits.
+  // workgroups of 256 rows against 256 of 128); with 256-row workgroups,
+  // a thin last round per XCD runs as 128-row halves (S = 56160, 40 heads:
+  // 1100 items per XCD, 34 rounds of 32 and 12 left, run as 24 halves).
+  // All of these give the same bits.
   const int64_t p8_items = (int64_t)p.B * p.H * ((p.Sq + kP8BM - 1) / kP8BM);
   const int64_t h8_items = (int64_t)p.B * p.H * ((p.Sq + kH8BM - 1) / kH8BM);
   if (prefer_two_waves(p8_items, h8_items, p.n_cu)) {
     p.n_qblk = (p.Sq + kP8BM - 1) / kP8BM;
     p.n_items = (int32_t)p8_items;
+    p.n_tail = tail_halves(p8_items, p.n_cu);
+    if (p.n_tail > 0) {
+      const int64_t blocks = p8_items + (int64_t)kXcdCount * p.n_tail;
+      hipLaunchKernelGGL(attn_fwd_bf16_p8t_kernel, dim3((unsigned)blocks), dim3(kP8Waves * 64), 0,
+                         s, p);
+      return hipGetLastError();
+    }
     hipLaunchKernelGGL(attn_fwd_bf16_p8_kernel, dim3(p.n_items), dim3(kP8Waves * 64), 0, s, p);
     return hipGetLastError();
   }

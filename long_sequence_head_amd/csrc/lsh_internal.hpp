@@ -42,6 +42,9 @@ struct AttnParams {
   // folded into a running result) instead of overwriting them
   int32_t accumulate;
   int32_t n_cu;       // compute units of the device (0: assume 256)
+  // dense 256-row launches: the last n_tail items of each XCD's range run
+  // as two 128-row halves (0: none)
+  int32_t n_tail;
 };
 
 enum class DType : int { F32 = 0, BF16 = 1 };
@@ -109,6 +112,23 @@ inline bool prefer_two_waves(int64_t items_big, int64_t items_small, int n_cu) {
   const int64_t r_big = (items_big + cus - 1) / cus;
   const int64_t r_small = (items_small + cus - 1) / cus;
   return 5 * r_big <= 3 * r_small;
+}
+
+// Workgroups go to the 8 XCDs in turn, and the dense kernels give XCD x the
+// contiguous items x * per .. x * per + per - 1 (per = items / 8). With one
+// 256-row workgroup per CU, an XCD's last round holds per % (CUs per XCD)
+// of them and leaves the other CUs idle. When that remainder is at most
+// half an XCD's CUs, running those items as twice as many 128-row halves
+// (about 3/5 of the time each) ends the round sooner. Returns the number of
+// items per XCD to split, or 0 (also when the items or the CUs do not split
+// evenly over the XCDs).
+inline int32_t tail_halves(int64_t items_big, int n_cu) {
+  constexpr int64_t kX = 8;
+  const int64_t cus = n_cu > 0 ? n_cu : 256;
+  if (cus % kX != 0 || items_big % kX != 0) return 0;
+  const int64_t per = items_big / kX, cu_x = cus / kX;
+  const int64_t r = per % cu_x;
+  return (r > 0 && 2 * r <= cu_x && per > cu_x) ? (int32_t)r : 0;
 }
 
 // Enqueues the three backward kernels (row statistics, dK/dV, dQ).

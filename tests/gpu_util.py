@@ -31,6 +31,27 @@ U_BF16 = 2.0 ** -8   # unit roundoff of bfloat16 (round to nearest even)
 SIGMA_ALARM = 8.0    # bf16 O errors beyond this many sigma of weight rounding fail
 
 
+def dense_bf16_launch(B: int, Sq: int, H: int, n_cu: int = 256):
+    """Which dense bf16 forward kernel a call of this shape launches, as
+    ("256-row", blocks), ("256-row, split tail", blocks, halves per XCD) or
+    ("128-row", blocks): the launcher's rule, restated so that tests can
+    check that their shapes reach the path they are meant for.
+    256-row items win unless their rounds over the CUs are more than 3/5 of
+    the 128-row kernel's; then, when the items and CUs split evenly over the
+    8 XCDs and each XCD's last round holds at most half its CUs' worth of
+    items (with more than one round), those items run as 128-row halves."""
+    big = B * H * -(-Sq // 256)
+    small = B * H * -(-Sq // 128)
+    if not 5 * -(-big // n_cu) <= 3 * -(-small // n_cu):
+        return ("128-row", small)
+    if n_cu % 8 == 0 and big % 8 == 0:
+        per, cu_x = big // 8, n_cu // 8
+        r = per % cu_x
+        if 0 < r and 2 * r <= cu_x and per > cu_x:
+            return ("256-row, split tail", big + 8 * r, r)
+    return ("256-row", big)
+
+
 def torch():
     import torch as t
     return t

@@ -282,6 +282,42 @@ def test_large_grid_strided(L):
         assert t.equal(o[:, :, sl], o4) and t.equal(lse[:, sl], l4), f"heads {h0}..{h0 + 3}"
 
 
+def test_tail_halves_bitwise(L):
+    """H=32, S=4133: 544 items of 256 rows, 68 per XCD (the 4 heads 4x ..
+    4x + 3 of XCD x); 64 run whole and the last 4 (query blocks 13..16 of
+    head 4x + 3, the last holding 37 rows, so its second half none) as
+    128-row halves in the same launch (the empty half returns at once).
+    Every head bit-identical to calls on 4 heads at a time (the 128-row
+    kernel); split rows of heads 3 and 31 and whole rows of heads 0 and 3
+    against the oracle."""
+    G.announce("256-row grid with split tail")
+    t = G.torch()
+    S, H = 4133, 32
+    plan = G.dense_bf16_launch(1, S, H)
+    assert plan == ("256-row, split tail", 576, 4), plan
+    assert G.dense_bf16_launch(1, S, 4)[0] == "128-row"
+    q, k, v = I.make_custom((1, S, H, 128), (1, S, H, 128), "bf16", seed=96)
+    qg, kg, vg = G.to_gpu(q, "bf16"), G.to_gpu(k, "bf16"), G.to_gpu(v, "bf16")
+    o, lse = G.poisoned_outputs(1, S, H)
+    L.attn_fwd(qg, kg, vg, o=o, lse=lse)
+    t.cuda.synchronize()
+    assert not t.isnan(o).any() and not t.isnan(lse).any(), "unwritten output"
+    for h0 in range(0, H, 4):
+        sl = slice(h0, h0 + 4)
+        o4, l4 = L.attn_fwd(qg[:, :, sl].contiguous(), kg[:, :, sl].contiguous(),
+                            vg[:, :, sl].contiguous())
+        assert t.equal(o[:, :, sl], o4) and t.equal(lse[:, sl], l4), f"heads {h0}..{h0 + 3}"
+    rows = np.unique(np.concatenate([np.arange(0, 64), np.arange(3328, 3328 + 64),
+                                     np.arange(3520, 3600), np.arange(4090, S)]))
+    heads = [0, 3, 31]
+    o_ref, lse_ref = oracle.attention_ref(q.values, k.values, v.values, 1 / math.sqrt(128),
+                                          heads=heads, rows=rows)
+    ridx = t.from_numpy(rows).cuda()
+    og = o.index_select(1, ridx).cpu().numpy()[:, :, heads]
+    lg = lse.index_select(2, ridx).cpu().numpy()[:, heads]
+    G.check("split tail", "bf16", og, lg, o_ref[:, :, heads], lse_ref[:, heads])
+
+
 def test_permute_bit_exact(L):
     G.announce("permute")
     t = G.torch()
@@ -378,8 +414,9 @@ def test_partial_accumulate_small(L, dtype):
 
 
 def test_partial_accumulate_large_grid(L):
-    """H=32, Sq=4133: each fold is a 544-workgroup launch of the 256-row
-    kernel. Three blocks (1500, 1500, 37 keys) against the
+    """H=32, Sq=4133: each fold is a launch of 544 items of 256 rows (the
+    last 4 of each XCD's 68 as 128-row halves). Three blocks (1500, 1500,
+    37 keys) against the
     oracle on heads 0 and 31; the first fold bit-identical to
     lsh_attn_partial."""
     G.announce("partial accumulate, large grid")
@@ -486,8 +523,8 @@ def test_blocksparse_all_ones_equals_dense_bitwise(L, dtype):
 
 def test_blocksparse_all_ones_large_grid_equals_dense_bitwise(L):
     """H=32, S=4133: 1056 sparse workgroups, two to a CU, against the dense
-    call (544 workgroups of 256 rows: the 256-row kernel); the last
-    key block holds 37 keys."""
+    call (544 items of 256 rows, 68 per XCD: 64 run whole and the last 4
+    as 128-row halves); the last key block holds 37 keys."""
     G.announce("sparse all-ones, large grid")
     t = G.torch()
     S, H = 4133, 32
@@ -571,9 +608,10 @@ def test_blocksparse_schedule(L, case):
 
 @pytest.mark.parametrize("Skv", [1, 63, 64, 65, 128, 129, 191, 333, 1000, 4097])
 def test_large_grid_ragged_keys(L, Skv):
-    """A grid of 1032 workgroups (several per CU over time): sampled query
-    rows (incl. the ragged last query tile) against the oracle over key
-    counts that end mid-tile, at one tile, and below the prefetch depth."""
+    """Sq=16400, H=8: 520 items of 256 rows, 65 per XCD (two rounds of 32,
+    the last item of each XCD as 128-row halves): sampled query rows (incl.
+    the ragged last query tile) against the oracle over key counts that end
+    mid-tile, at one tile, and below the prefetch depth."""
     G.announce(f"large grid ragged Skv={Skv}")
     t = G.torch()
     B, Sq, H = 1, 16400, 8

@@ -36,3 +36,22 @@ def test_bf16_weight_sigma_empty_rows_are_zero():
     o, lse = oracle.attention_ref(q, k, v, 0.5, block_mask=mask)
     sig = G.bf16_weight_sigma(oracle, q, k, v, 0.5, lse, block_mask=mask)
     assert np.all(sig[:, 128:] == 0) and np.all(sig[:, :128] > 0)
+
+
+def test_dense_bf16_launch_cases():
+    """The launch rule on the workloads' shapes and on the shapes the GPU
+    tests use to reach each path (256 CUs)."""
+    # 56160 queries x 40 heads: 8800 items, 1100 per XCD = 34 rounds + 12
+    assert G.dense_bf16_launch(1, 56160, 40) == ("256-row, split tail", 8800 + 8 * 12, 12)
+    # head chunks of S = 32760: 128 blocks per head, rounds of 32 per XCD
+    assert G.dense_bf16_launch(1, 32760, 16) == ("256-row", 2048)
+    assert G.dense_bf16_launch(1, 32760, 12) == ("256-row", 1536)
+    assert G.dense_bf16_launch(1, 32760, 40) == ("256-row", 5120)
+    # a ring round: 128 items of 256 rows would leave half the CUs idle
+    assert G.dense_bf16_launch(1, 4096, 8) == ("128-row", 256)
+    # 544 items, 68 per XCD: the last 4 of each as halves
+    assert G.dense_bf16_launch(1, 4133, 32) == ("256-row, split tail", 576, 4)
+    # remainders above half an XCD, or one round only, stay whole
+    assert G.dense_bf16_launch(1, 256 * 52, 8) == ("256-row", 416)
+    assert G.dense_bf16_launch(1, 16384, 8) == ("256-row", 512)
+    assert G.dense_bf16_launch(1, 16400, 8) == ("256-row, split tail", 528, 1)
