@@ -17,7 +17,8 @@
 //    v_mfma_f32_16x16x32_bf16, key tiles filled by LDS DMA into rings of
 //    slots, a software pipeline of 32-key units per wavefront; three
 //    instances (dense 256-row and 128-row workgroups, block-sparse) that
-//    give the same bits;
+//    give the same bits, launched alone or, for a dense grid with a thin
+//    last round, 256-row and 128-row ones in one launch;
 //  * fp32 inputs: one template (attn_fwd_f32_kernel) on
 //    v_mfma_f32_32x32x2_f32, the key tiles of a query block split between
 //    two wavefronts and merged at the end; dense and block-sparse give the
