@@ -282,26 +282,40 @@ def test_large_grid_strided(L):
         assert t.equal(o[:, :, sl], o4) and t.equal(lse[:, sl], l4), f"heads {h0}..{h0 + 3}"
 
 
-def test_tail_halves_bitwise(L):
-    """H=32, S=4133: 544 items of 256 rows, 68 per XCD (the 4 heads 4x ..
-    4x + 3 of XCD x); 64 run whole and the last 4 (query blocks 13..16 of
-    head 4x + 3, the last holding 37 rows, so its second half none) as
-    128-row halves in the same launch (the empty half returns at once).
-    Every head bit-identical to calls on 4 heads at a time (the 128-row
-    kernel); split rows of heads 3 and 31 and whole rows of heads 0 and 3
+@pytest.mark.parametrize("B,H,packed", [(1, 32, False), (2, 16, True)], ids=["B1H32", "B2H16-packed"])
+def test_tail_halves_bitwise(L, B, H, packed):
+    """S=4133 with B*H = 32: 544 items of 256 rows, 68 per XCD (the 4
+    (b, h) pairs 4x .. 4x + 3 of XCD x; with B=2 the upper XCDs hold batch
+    entry 1); 64 run whole and the last 4 (query blocks 13..16 of pair
+    4x + 3, the last holding 37 rows, so its second half none) as 128-row
+    halves in the same launch (the empty half returns at once). The B=2
+    case reads Q, K, V as views of one packed [B, S, 3, H, D] buffer and
+    writes O into a wider one. Every head bit-identical to calls on 4 heads
+    at a time (no split: the 128-row kernel for B=1, the plain 256-row one
+    for B=2); split and whole rows of the first and last batch entry
     against the oracle."""
-    G.announce("256-row grid with split tail")
+    G.announce(f"256-row grid with split tail B={B} H={H} packed={packed}")
     t = G.torch()
-    S, H = 4133, 32
-    plan = G.dense_bf16_launch(1, S, H)
+    S, D = 4133, 128
+    plan = G.dense_bf16_launch(B, S, H)
     assert plan == ("256-row, split tail", 576, 4), plan
-    assert G.dense_bf16_launch(1, S, 4)[0] == "128-row"
-    q, k, v = I.make_custom((1, S, H, 128), (1, S, H, 128), "bf16", seed=96)
+    assert G.dense_bf16_launch(B, S, 4)[0] in ("128-row", "256-row")   # no split tail
+    q, k, v = I.make_custom((B, S, H, D), (B, S, H, D), "bf16", seed=96 + B)
     qg, kg, vg = G.to_gpu(q, "bf16"), G.to_gpu(k, "bf16"), G.to_gpu(v, "bf16")
-    o, lse = G.poisoned_outputs(1, S, H)
+    if packed:
+        buf = t.zeros((B, S, 3, H, D), dtype=t.bfloat16, device="cuda")
+        buf[:, :, 0], buf[:, :, 1], buf[:, :, 2] = qg, kg, vg
+        qg, kg, vg = buf[:, :, 0], buf[:, :, 1], buf[:, :, 2]
+        wide = t.full((B, S, H + 2, D), float("nan"), dtype=t.float32, device="cuda")
+        o = wide[:, :, 1:H + 1]
+        lse = t.full((B, H, S), float("nan"), dtype=t.float32, device="cuda")
+    else:
+        o, lse = G.poisoned_outputs(B, S, H)
     L.attn_fwd(qg, kg, vg, o=o, lse=lse)
     t.cuda.synchronize()
     assert not t.isnan(o).any() and not t.isnan(lse).any(), "unwritten output"
+    if packed:
+        assert t.isnan(wide[:, :, 0]).all() and t.isnan(wide[:, :, H + 1]).all(), "wrote outside O"
     for h0 in range(0, H, 4):
         sl = slice(h0, h0 + 4)
         o4, l4 = L.attn_fwd(qg[:, :, sl].contiguous(), kg[:, :, sl].contiguous(),
@@ -309,8 +323,8 @@ def test_tail_halves_bitwise(L):
         assert t.equal(o[:, :, sl], o4) and t.equal(lse[:, sl], l4), f"heads {h0}..{h0 + 3}"
     rows = np.unique(np.concatenate([np.arange(0, 64), np.arange(3328, 3328 + 64),
                                      np.arange(3520, 3600), np.arange(4090, S)]))
-    heads = [0, 3, 31]
-    o_ref, lse_ref = oracle.attention_ref(q.values, k.values, v.values, 1 / math.sqrt(128),
+    heads = [0, 3, H - 1]
+    o_ref, lse_ref = oracle.attention_ref(q.values, k.values, v.values, 1 / math.sqrt(D),
                                           heads=heads, rows=rows)
     ridx = t.from_numpy(rows).cuda()
     og = o.index_select(1, ridx).cpu().numpy()[:, :, heads]
