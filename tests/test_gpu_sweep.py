@@ -1,0 +1,124 @@
+"""Seeded sweep of the forward entry points (lsh_attn_fwd, lsh_attn_partial,
+lsh_attn_fwd_blocksparse) over random shapes, dtypes, batch sizes, memory
+layouts, softmax scales and block masks, against the fp64 oracle on sampled
+query rows (always including the first row and the whole last 128-row tile)
+of every head. Every dense case is also run through the block-sparse path
+with an all-ones mask, which must give the same bits.
+
+Layouts: contiguous [B, S, H, D]; K and V as views of one packed
+[B, S, 2, H, D] buffer with O written into a wider [B, S, H + 2, D] one
+(the columns beside it must stay untouched); head-major views (a
+[B, H, S, D] buffer seen as [B, S, H, D], the layout a head permute
+produces). The case list is drawn from a fixed seed in this file."""
+import math
+
+import numpy as np
+import pytest
+
+import lsh_inputs as I
+import oracle
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+
+
+def _cases(n):
+    rng = np.random.default_rng(20261203)
+    out = []
+    for i in range(n):
+        entry = ("fwd", "partial", "sparse")[i % 3]
+        dtype = "f32" if i % 4 == 3 else "bf16"
+        B = int(rng.integers(1, 4))
+        H = int(rng.integers(1, 13))
+        short = rng.random() < 0.4
+        Sq = int(rng.integers(1, 300)) if short else int(rng.integers(300, 2600))
+        Skv = int(rng.integers(1, 300)) if rng.random() < 0.3 else int(rng.integers(300, 4200))
+        layout = ("contig", "packed", "headmajor")[int(rng.integers(0, 3))]
+        scale = None if rng.random() < 0.5 else float(rng.uniform(0.03, 0.3))
+        density = float(rng.uniform(0.1, 0.9))
+        out.append((i, entry, dtype, B, H, Sq, Skv, layout, scale, density))
+    # a partial over an empty key block
+    out.append((n, "partial", "bf16", 2, 3, 130, 0, "contig", None, 0.0))
+    return out
+
+
+CASES = _cases(40)
+
+
+@pytest.fixture(scope="module")
+def L():
+    import long_sequence_head_amd as lsh
+    lsh.load()
+    return lsh
+
+
+def _layout(t, x, layout, dtype):
+    """GPU view of lsh_inputs tensor x ([B, S, H, D]) in the given layout."""
+    g = G.to_gpu(x, dtype)
+    if layout == "headmajor":
+        hm = g.permute(0, 2, 1, 3).contiguous()          # [B, H, S, D] storage
+        return hm.permute(0, 2, 1, 3)                     # seen as [B, S, H, D]
+    return g
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c[:8])))
+def test_sweep_vs_oracle(L, case):
+    i, entry, dtype, B, H, Sq, Skv, layout, scale, density = case
+    G.announce(f"sweep {case}")
+    t = G.torch()
+    q, k, v = I.make_custom((B, Sq, H, D), (B, Skv, H, D), dtype, seed=1000 + i)
+    sc = 1.0 / math.sqrt(D) if scale is None else scale
+    qg = _layout(t, q, layout, dtype)
+    if Skv == 0:
+        kg = vg = None
+    elif layout == "packed":
+        kv = t.zeros((B, Skv, 2, H, D), dtype=t.bfloat16 if dtype == "bf16" else t.float32,
+                     device="cuda")
+        kv[:, :, 0], kv[:, :, 1] = G.to_gpu(k, dtype), G.to_gpu(v, dtype)
+        kg, vg = kv[:, :, 0], kv[:, :, 1]
+    else:
+        kg, vg = _layout(t, k, layout, dtype), _layout(t, v, layout, dtype)
+    if layout == "packed":
+        wide = t.full((B, Sq, H + 2, D), float("nan"), dtype=t.float32, device="cuda")
+        o = wide[:, :, 1:H + 1]
+        lse = t.full((B, H, Sq), float("nan"), dtype=t.float32, device="cuda")
+    else:
+        o, lse = G.poisoned_outputs(B, Sq, H)
+
+    mask = None
+    nqb, nkb = -(-Sq // 128), -(-max(Skv, 1) // 128)
+    if entry == "fwd":
+        L.attn_fwd(qg, kg, vg, scale=scale, o=o, lse=lse)
+    elif entry == "partial":
+        L.attn_partial(qg, kg, vg, scale=scale, o=o, lse=lse)
+    else:
+        rng = np.random.default_rng(5000 + i)
+        mask = (rng.random((B, H, nqb, nkb)) < density).astype(np.uint8)
+        mask[0, 0, 0, :] = 0                       # a query block with no kept key block
+        L.attn_fwd_blocksparse(qg, kg, vg, t.from_numpy(mask).cuda(), scale=scale, o=o, lse=lse)
+    t.cuda.synchronize()
+    assert not t.isnan(o).any() and not t.isnan(lse).any(), "unwritten output"
+    if layout == "packed":
+        assert t.isnan(wide[:, :, 0]).all() and t.isnan(wide[:, :, H + 1]).all(), "wrote outside O"
+
+    if Skv == 0:
+        assert t.equal(o, t.zeros_like(o)), "empty key block: O must be 0"
+        assert t.isneginf(lse).all(), "empty key block: LSE must be -inf"
+        return
+
+    if entry == "fwd":
+        ones = t.ones((B, H, nqb, nkb), dtype=t.uint8, device="cuda")
+        o1, l1 = L.attn_fwd_blocksparse(qg, kg, vg, ones, scale=scale)
+        assert t.equal(o1, o.contiguous()) and t.equal(l1, lse), "all-ones mask != dense bits"
+
+    rows = I.sample_rows(Sq, 48, seed=i)
+    kw = dict(rows=rows) if mask is None else dict(rows=rows, block_mask=mask)
+    o_ref, lse_ref = oracle.attention_ref(q.values, k.values, v.values, sc, **kw)
+    sig = None
+    if dtype == "bf16":
+        sig = G.bf16_weight_sigma(oracle, q.values, k.values, v.values, sc, lse_ref, **kw)
+    ridx = t.from_numpy(rows).cuda()
+    G.check(f"sweep {i}", dtype, o.index_select(1, ridx).cpu().numpy(),
+            lse.index_select(2, ridx).cpu().numpy(), o_ref, lse_ref, sigma=sig)
