@@ -9,7 +9,10 @@ Layouts: contiguous [B, S, H, D]; K and V as views of one packed
 [B, S, 2, H, D] buffer with O written into a wider [B, S, H + 2, D] one
 (the columns beside it must stay untouched); head-major views (a
 [B, H, S, D] buffer seen as [B, S, H, D], the layout a head permute
-produces). The case list is drawn from a fixed seed in this file."""
+produces). The case list is drawn from a fixed seed in this file.
+
+A second sweep runs lsh_attn_bwd after the library's forward on random
+shapes, scales and layouts, every gradient against the oracle's."""
 import math
 
 import numpy as np
@@ -122,3 +125,45 @@ def test_sweep_vs_oracle(L, case):
     ridx = t.from_numpy(rows).cuda()
     G.check(f"sweep {i}", dtype, o.index_select(1, ridx).cpu().numpy(),
             lse.index_select(2, ridx).cpu().numpy(), o_ref, lse_ref, sigma=sig)
+
+
+def _bwd_cases(n):
+    rng = np.random.default_rng(20261204)
+    out = []
+    for i in range(n):
+        B = int(rng.integers(1, 4))
+        H = int(rng.integers(1, 7))
+        Sq = int(rng.integers(1, 200)) if rng.random() < 0.3 else int(rng.integers(200, 1500))
+        Skv = int(rng.integers(1, 200)) if rng.random() < 0.3 else int(rng.integers(200, 1500))
+        layout = ("contig", "headmajor")[int(rng.integers(0, 2))]
+        scale = None if rng.random() < 0.5 else float(rng.uniform(0.03, 0.3))
+        out.append((i, B, H, Sq, Skv, layout, scale))
+    return out
+
+
+BWD_CASES = _bwd_cases(16)
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "-".join(map(str, c[:6])))
+def test_bwd_sweep_vs_oracle(L, case):
+    """lsh_attn_bwd after the library's own forward, on random shapes,
+    scales and layouts (contiguous, or head-major views of Q, K, V and dO),
+    with dQ, dK and dV written into NaN-filled buffers: every gradient
+    against the oracle's (each within 2e-2 of its largest magnitude)."""
+    i, B, H, Sq, Skv, layout, scale = case
+    G.announce(f"bwd sweep {case}")
+    t = G.torch()
+    q, k, v = I.make_custom((B, Sq, H, D), (B, Skv, H, D), "bf16", seed=3000 + i)
+    do = I.make_custom_dout((B, Sq, H, D), "bf16", seed=3000 + i)
+    qg, kg, vg, dog = (_layout(t, x, layout, "bf16") for x in (q, k, v, do))
+    sc = 1.0 / math.sqrt(D) if scale is None else scale
+    o, lse = L.attn_fwd(qg, kg, vg, scale=scale)
+    dq = t.full((B, Sq, H, D), float("nan"), dtype=t.float32, device="cuda")
+    dk = t.full((B, Skv, H, D), float("nan"), dtype=t.float32, device="cuda")
+    dv = t.full((B, Skv, H, D), float("nan"), dtype=t.float32, device="cuda")
+    L.attn_bwd(qg, kg, vg, dog, o, lse, scale=scale, dq=dq, dk=dk, dv=dv)
+    t.cuda.synchronize()
+    for name, x in (("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert not t.isnan(x).any(), f"unwritten {name}"
+    ref = oracle.attention_bwd_ref(q.values, k.values, v.values, do.values, sc)
+    G.check_grads(f"bwd sweep {i}", [x.cpu().numpy() for x in (dq, dk, dv)], ref)
