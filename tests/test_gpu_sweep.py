@@ -11,8 +11,12 @@ Layouts: contiguous [B, S, H, D]; K and V as views of one packed
 [B, H, S, D] buffer seen as [B, S, H, D], the layout a head permute
 produces). The case list is drawn from a fixed seed in this file.
 
-A second sweep runs lsh_attn_bwd after the library's forward on random
-shapes, scales and layouts, every gradient against the oracle's."""
+Further sweeps: lsh_attn_bwd after the library's forward on random shapes,
+scales and layouts, every gradient against the oracle's; the head-chunked
+pipeline over random uneven chunkings, bit for bit against the unchunked
+call; and ring rounds over random key-block splits (empty blocks
+included), folded on arrival and merged from partials, against the
+oracle."""
 import math
 
 import numpy as np
@@ -167,3 +171,96 @@ def test_bwd_sweep_vs_oracle(L, case):
         assert not t.isnan(x).any(), f"unwritten {name}"
     ref = oracle.attention_bwd_ref(q.values, k.values, v.values, do.values, sc)
     G.check_grads(f"bwd sweep {i}", [x.cpu().numpy() for x in (dq, dk, dv)], ref)
+
+
+def _chunk_cases(n):
+    rng = np.random.default_rng(20261205)
+    out = []
+    for i in range(n):
+        H = int(rng.integers(2, 21))
+        n_chunks = int(rng.integers(1, min(H, 6) + 1))
+        cuts = np.sort(rng.choice(np.arange(1, H), size=n_chunks - 1, replace=False))
+        chunks = np.diff(np.concatenate([[0], cuts, [H]])).astype(int).tolist()
+        B = int(rng.integers(1, 3))
+        S = int(rng.integers(1, 2000))
+        dtype = "f32" if i % 3 == 2 else "bf16"
+        out.append((i, B, S, H, tuple(chunks), dtype))
+    return out
+
+
+CHUNK_CASES = _chunk_cases(12)
+
+
+@pytest.mark.parametrize("case", CHUNK_CASES, ids=lambda c: "-".join(map(str, c[:4])) + "-" + c[5])
+def test_chunked_sweep_bit_identical(L, case):
+    """lsh_attn_fwd_chunked over random uneven head chunkings (1 to 5
+    chunks), both dtypes and ragged S: every element equal to the unchunked
+    call, run on the current stream and a second one for the permutes."""
+    i, B, S, H, chunks, dtype = case
+    G.announce(f"chunked sweep {case}")
+    t = G.torch()
+    q, k, v = I.make_custom((B, S, H, D), (B, S, H, D), dtype, seed=4000 + i)
+    qg, kg, vg = G.to_gpu(q, dtype), G.to_gpu(k, dtype), G.to_gpu(v, dtype)
+    o1, l1 = L.attn_fwd(qg, kg, vg)
+    o2, l2 = G.poisoned_outputs(B, S, H)
+    L.attn_fwd_chunked(qg, kg, vg, list(chunks), o=o2, lse=l2)
+    t.cuda.synchronize()
+    assert t.equal(o1, o2) and t.equal(l1, l2), f"chunks {chunks}"
+
+
+def _fold_cases(n):
+    rng = np.random.default_rng(20261206)
+    out = []
+    for i in range(n):
+        B = int(rng.integers(1, 3))
+        H = int(rng.integers(1, 9))
+        Sq = int(rng.integers(1, 1500))
+        n_blocks = int(rng.integers(1, 7))
+        sizes = [int(rng.integers(0, 900)) if rng.random() < 0.8 else 0 for _ in range(n_blocks)]
+        if sum(sizes) == 0:
+            sizes[0] = 1
+        dtype = "f32" if i % 4 == 3 else "bf16"
+        out.append((i, B, H, Sq, tuple(sizes), dtype))
+    return out
+
+
+FOLD_CASES = _fold_cases(12)
+
+
+@pytest.mark.parametrize("case", FOLD_CASES, ids=lambda c: "-".join(map(str, c[:4])) + "-" + c[5])
+def test_ring_fold_and_merge_sweep(L, case):
+    """A ring round per key block, in two ways: the blocks folded into a
+    running result on arrival (lsh_attn_partial_accumulate, empty blocks
+    included), and one lsh_attn_partial per non-empty block merged by
+    lsh_lse_merge. Both against the oracle over all the keys on sampled
+    rows of every head; the first non-empty fold equals lsh_attn_partial
+    bit for bit."""
+    i, B, H, Sq, sizes, dtype = case
+    G.announce(f"fold sweep {case}")
+    t = G.torch()
+    Skv = sum(sizes)
+    q, k, v = I.make_custom((B, Sq, H, D), (B, Skv, H, D), dtype, seed=6000 + i)
+    qg, kg, vg = G.to_gpu(q, dtype), G.to_gpu(k, dtype), G.to_gpu(v, dtype)
+    o = t.zeros((B, Sq, H, D), dtype=t.float32, device="cuda")
+    lse = t.full((B, H, Sq), float("-inf"), dtype=t.float32, device="cuda")
+    parts_o, parts_l = [], []
+    a, first = 0, True
+    for n in sizes:
+        kb, vb = kg[:, a:a + n], vg[:, a:a + n]
+        L.attn_partial_accumulate(qg, kb, vb, o, lse)
+        if n > 0:
+            po, pl = L.attn_partial(qg, kb, vb)
+            parts_o.append(po)
+            parts_l.append(pl)
+            if first:
+                assert t.equal(o, po) and t.equal(lse, pl), "first fold"
+                first = False
+        a += n
+    om, lm = L.lse_merge(t.stack(parts_o).contiguous(), t.stack(parts_l).contiguous())
+    t.cuda.synchronize()
+    rows = I.sample_rows(Sq, 48, seed=i)
+    o_ref, lse_ref = oracle.attention_ref(q.values, k.values, v.values, 1 / math.sqrt(D), rows=rows)
+    ridx = t.from_numpy(rows).cuda()
+    for name, oo, ll in (("fold", o, lse), ("merge", om, lm)):
+        G.check(f"{name} sweep {i}", dtype, oo.index_select(1, ridx).cpu().numpy(),
+                ll.index_select(2, ridx).cpu().numpy(), o_ref, lse_ref)
