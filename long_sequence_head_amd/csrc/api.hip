@@ -31,6 +31,17 @@ int elem_bytes(int32_t dtype) { return dtype == LSH_F32 ? 4 : 2; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Size and span checks multiply caller-given 64-bit values (sizes below
+// 2^30, strides of any value); they are formed in 128 bits so that no
+// product wraps.
+using wide_t = __int128;
+inline wide_t W(int64_t x) { return static_cast<wide_t>(x); }
+// a * b * c >= limit for factors >= 1 of any size (limit below 2^31)
+inline bool prod3_ge(int64_t a, int64_t b, int64_t c, int64_t limit) {
+  if (a >= limit || b >= limit || c >= limit) return true;
+  return W(a) * b * c >= limit;
+}
+
 constexpr int kMaxDevices = 64;
 std::mutex g_dev_mu;
 int g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
@@ -81,7 +92,8 @@ lsh_status validate_attn(const lsh_attn_args* a, bool allow_empty_kv, const char
   if (a->B >= lim || a->Sq >= lim || a->Skv >= lim || a->H >= lim)
     return fail(LSH_ERR_UNSUPPORTED, "%s: sizes must be below 2^30", fn);
   const int64_t qblocks = (a->Sq + 127) / 128;
-  if (a->B * a->H * qblocks >= ((int64_t)1 << 31) || a->B * a->Sq * a->H >= ((int64_t)1 << 31))
+  const wide_t big = W(1) << 31;
+  if (W(a->B) * a->H * qblocks >= big || W(a->B) * a->Sq * a->H >= big)
     return fail(LSH_ERR_UNSUPPORTED, "%s: B*Sq*H too large", fn);
   if (!a->q || !a->o || !a->lse) return fail(LSH_ERR_INVALID, "%s: q, o and lse must be non-NULL", fn);
   const bool need_kv = a->Skv > 0;
@@ -95,9 +107,9 @@ lsh_status validate_attn(const lsh_attn_args* a, bool allow_empty_kv, const char
   // bf16 K and V rows are read through buffer descriptors with 32-bit byte
   // offsets: one head's rows must span less than 2 GiB.
   if (a->dtype == LSH_BF16 && need_kv) {
-    const int64_t span_k = (a->Skv - 1) * a->k_stride[1] * eb + a->D * eb;
-    const int64_t span_v = (a->Skv - 1) * a->v_stride[1] * eb + a->D * eb;
-    if (span_k >= ((int64_t)1 << 31) || span_v >= ((int64_t)1 << 31))
+    const wide_t span_k = W(a->Skv - 1) * a->k_stride[1] * eb + W(a->D) * eb;
+    const wide_t span_v = W(a->Skv - 1) * a->v_stride[1] * eb + W(a->D) * eb;
+    if (span_k >= big || span_v >= big)
       return fail(LSH_ERR_UNSUPPORTED,
                   "%s: the K/V rows of one head span 2 GiB or more (Skv x key stride)", fn);
   }
@@ -164,11 +176,11 @@ lsh_status validate_bwd(const lsh_attn_bwd_args* a, const char* fn) {
   const int64_t lim = (int64_t)1 << 30;
   if (a->B >= lim || a->Sq >= lim || a->Skv >= lim || a->H >= lim)
     return fail(LSH_ERR_UNSUPPORTED, "%s: sizes must be below 2^30", fn);
-  const int64_t big = (int64_t)1 << 31;
-  const int64_t bh = a->B * a->H;
+  const wide_t big = W(1) << 31;
+  const wide_t bh = W(a->B) * a->H;
   if (bh * ((a->Sq + 127) / 128) >= big || bh * ((a->Skv + 127) / 128) >= big ||
       bh * ((a->Sq + lsh::kBwdQT - 1) / lsh::kBwdQT) * (lsh::kBwdQT / 16) >= big ||
-      a->B * a->Sq * a->H >= big || a->B * a->Skv * a->H >= big)
+      bh * a->Sq >= big || bh * a->Skv >= big)
     return fail(LSH_ERR_UNSUPPORTED, "%s: B*S*H too large", fn);
   const void* ptrs[9] = {a->q, a->k, a->v, a->dout, a->o, a->lse, a->dq, a->dk, a->dv};
   static const char* names[9] = {"q", "k", "v", "dout", "o", "lse", "dq", "dk", "dv"};
@@ -193,7 +205,7 @@ lsh_status validate_bwd(const lsh_attn_bwd_args* a, const char* fn) {
   // byte offsets: one head's rows of each must span less than 2 GiB.
   const int64_t rows[4] = {a->Sq, a->Skv, a->Skv, a->Sq};
   for (int t = 0; t < 4; ++t)
-    if ((rows[t] - 1) * strides[t][1] * 2 + a->D * 2 >= big)
+    if (W(rows[t] - 1) * strides[t][1] * 2 + W(a->D) * 2 >= big)
       return fail(LSH_ERR_UNSUPPORTED, "%s: the rows of one head span 2 GiB or more", fn);
   return LSH_OK;
 }
@@ -487,7 +499,8 @@ lsh_status lsh_lse_merge(const float* o_parts, const float* lse_parts, int32_t n
   if (B < 1 || Sq < 1 || H < 1 || D < 1) return fail(LSH_ERR_INVALID, "%s: sizes must be >= 1", fn);
   if (D != LSH_HEAD_DIM)
     return fail(LSH_ERR_UNSUPPORTED, "%s: head_dim %lld is not supported", fn, (long long)D);
-  if (B * Sq * H >= ((int64_t)1 << 31)) return fail(LSH_ERR_UNSUPPORTED, "%s: too many rows", fn);
+  if (prod3_ge(B, Sq, H, (int64_t)1 << 31))
+    return fail(LSH_ERR_UNSUPPORTED, "%s: too many rows", fn);
   if (!aligned16(o_parts) || !aligned16(o) || !aligned16(lse_parts) || !aligned16(lse))
     return fail(LSH_ERR_INVALID, "%s: pointers must be 16-byte aligned", fn);
   lsh_status st = device_check_impl();
@@ -507,8 +520,9 @@ lsh_status lsh_head_permute(const void* src, void* dst, int32_t dtype, int64_t B
     return fail(LSH_ERR_INVALID, "%s: head range [%d, %d) outside [0, %lld)", fn, h0, h0 + hc,
                 (long long)H);
   const int eb = elem_bytes(dtype);
-  if ((D * eb) % 16 != 0) return fail(LSH_ERR_INVALID, "%s: D * element size must be a multiple of 16", fn);
-  if (S * (D * eb / 16) >= ((int64_t)1 << 31) || B * hc > 65535)
+  if ((W(D) * eb) % 16 != 0)
+    return fail(LSH_ERR_INVALID, "%s: D * element size must be a multiple of 16", fn);
+  if (W(S) * (W(D) * eb / 16) >= (W(1) << 31) || W(B) * hc > 65535)
     return fail(LSH_ERR_UNSUPPORTED, "%s: shape too large", fn);
   if (!aligned16(src) || !aligned16(dst)) return fail(LSH_ERR_INVALID, "%s: pointers must be 16-byte aligned", fn);
   lsh_status st = device_check_impl();
