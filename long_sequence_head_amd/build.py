@@ -81,7 +81,32 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     if missing:
         raise RuntimeError("liblsh.so has undefined symbols of its own:\n" + "\n".join(missing))
     os.replace(tmp, out)
+    build_c_abi_check()
     return out
+
+
+C_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi", "lsh_c_abi_check.c")
+C_CHECK_BIN = os.path.join(LIBDIR, "lsh_c_abi_check")
+
+
+def build_c_abi_check() -> str:
+    """Compiles the plain-C user of the library (tests/c_abi) with the host
+    C compiler against include/lsh.h and the HIP runtime; it finds liblsh.so
+    beside itself."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no host C compiler for the C ABI check")
+    tmp = C_CHECK_BIN + ".tmp"
+    cmd = [cc, "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", INCLUDE, "-I", os.path.join(rocm, "include"), C_CHECK_SRC,
+           "-L", LIBDIR, "-llsh", "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-lm",
+           "-Wl,-rpath,$ORIGIN", "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"C ABI check build failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    os.replace(tmp, C_CHECK_BIN)
+    return C_CHECK_BIN
 
 
 if __name__ == "__main__":
