@@ -1,7 +1,9 @@
 """The plain-C user of the library (tests/c_abi/lsh_c_abi_check.c, built
-beside liblsh.so by the build step) runs on the GPU: a closed form through
-lsh_attn_fwd for bf16 and float32 inputs in two layouts, and a refused
-argument block, using only include/lsh.h and the HIP runtime."""
+beside liblsh.so by the build step) runs on the GPU, using only
+include/lsh.h and the HIP runtime: a closed form (K = 0) through the
+forward (bf16 and float32, two layouts), partials with the LSE merge and
+with folding on arrival, the head permute, the allocation-free
+block-sparse call, the backward, and a refused argument block."""
 import os
 import subprocess
 
